@@ -1,0 +1,220 @@
+"""Benchmark of the gfx950 vision PatchEmbed: one JSON line on stdout.
+
+A step is one PatchEmbed forward (gather + matrix product + epilogue, one kernel launch per
+<= 64 items) over one batch of synthetic input already resident in HBM. The timed region is
+K steps captured back to back in a HIP graph and replayed once, bracketed by HIP events on the
+stream they run on; `eager_ms_per_step` gives the same K steps launched one by one from Python.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--extra 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "PatchEmbed patches/s + TFLOP/s (% bf16 MFMA peak) on 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_F32_MATRIX_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "vlm_vision_patch_amd", "csrc", f)
+                  for f in ("pe_kernels.hip", "pe_internal.h", "pe_api.cpp")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(wl):
+    """FLOPs and algorithmic HBM bytes of one step: unique input read once (one frame per image,
+    every frame of a video; patch rows as given), packed weight, bias, output."""
+    import workloads
+    esz = {"bf16": 2, "f32": 4}
+    n = sum(t * h * w for (t, h, w) in wl.grid)
+    flops = 2.0 * n * wl.k * wl.embed
+    inp = 1
+    for d in wl.input_shape:
+        inp *= d
+    byts = inp * esz[wl.in_dtype] + wl.embed * wl.k * esz[wl.w_dtype] + \
+        (wl.embed * esz[wl.w_dtype] if wl.bias else 0) + n * wl.embed * esz[wl.out_dtype]
+    return n, flops, byts
+
+
+def time_workload(idx, steps, warmup, graph=True):
+    import torch
+    import workloads
+    import vlm_vision_patch_amd as pe
+
+    wl = workloads.WORKLOADS[idx]
+    dev = torch.device("cuda:0")
+    x, w, b = workloads.generate(wl)
+    x, w = x.to(dev), w.to(dev)
+    b = b.to(dev) if b is not None else None
+    mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype])
+    grid, frames = [list(g) for g in wl.grid], list(wl.frames) or None
+    n, flops, byts = algorithmic(wl)
+    out = torch.empty((n, wl.embed), dtype=workloads.DTYPES[wl.out_dtype], device=dev)
+    s = torch.cuda.Stream(device=dev)   # default priority
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            mod(x, grid, frames, kind=wl.kind, out=out)
+        # eager: K launches from Python
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(steps):
+            mod(x, grid, frames, kind=wl.kind, out=out)
+        e1.record(s)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / steps
+    ms = eager_ms
+    timing = "K eager launches between HIP events"
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(steps):
+                mod(x, grid, frames, kind=wl.kind, out=out)
+        with torch.cuda.stream(s):
+            g.replay()                       # untimed: first replay uploads the graph
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+        timing = "K steps captured in one HIP graph, replayed once between HIP events"
+        del g
+    mod.close()
+    return dict(wl=wl, n=n, flops=flops, bytes=byts, ms=ms, eager_ms=eager_ms, timing=timing)
+
+
+def cpu_baseline(idx, min_seconds=10.0):
+    """The oracle, as it stands, timed on this host on repeats of the whole workload (or on its
+    first rows when one pass would exceed the bound)."""
+    import workloads
+    import oracle
+    wl = workloads.WORKLOADS[idx]
+    x, w, b = workloads.generate(wl)
+    n = sum(t * h * ww for (t, h, ww) in wl.grid)
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    rows = None
+    per_row = 2.0 * wl.k * wl.embed
+    if n * per_row > 2e11:      # more than ~30 s on 16 cores: time the first rows only
+        rows = list(range(int(2e11 / per_row)))
+    done, t0 = 0, time.perf_counter()
+    reps = 0
+    while True:
+        oracle.forward(x, w, b, grid=wl.grid, frames=list(wl.frames) or None, kind=wl.kind,
+                       order=wl.order, rows=rows, threads=threads)
+        done += n if rows is None else len(rows)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or rows is not None:
+            break
+    sample = ("%d passes over all %d rows" % (reps, n)) if rows is None else \
+        ("first %d of %d rows" % (len(rows), n))
+    return {"value": done / el, "unit": "patches/s", "cores": threads, "kind": "oracle",
+            "sample": "%s of %s (fp64 direct Conv3d, %d threads, %.1f s)" % (sample, wl.name, threads, el)}
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters, if they were
+    taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        rec = d.get(workload)
+        if rec and rec.get("kernel_hash") == kernel_hash():
+            return rec["bytes_per_launch"]
+    except Exception:
+        return None
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--extra", type=str, default="5",
+                    help="comma-separated further workloads reported under 'also' ('' for none)")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    r = time_workload(args.workload, args.steps, args.warmup)
+    wl = r["wl"]
+    t_s = r["ms"] / 1e3
+    tflops = r["flops"] / t_s / 1e12
+    gbs = r["bytes"] / t_s / 1e9
+    bf16 = wl.w_dtype == "bf16"
+    peak_fl = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_MATRIX_TFLOPS
+    ai = r["flops"] / r["bytes"]
+    ridge = peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if ai >= ridge else "hbm"
+    traffic = load_traffic("pe_fwd_kernel", wl.name)
+    roof = {"bound": bound,
+            "achieved": round(tflops if bound == "mfma" else gbs, 3),
+            "peak": peak_fl if bound == "mfma" else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+            "frac": round((tflops / peak_fl) if bound == "mfma" else (gbs / PEAK_HBM_GBS), 4),
+            "traffic": traffic,
+            "kernel": "pe_fwd_kernel",
+            "per_launch": {"flops": r["flops"], "alg_bytes": r["bytes"], "avg_us": round(r["ms"] * 1e3, 3)},
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    also = {}
+    for e in [int(v) for v in args.extra.split(",") if v.strip()]:
+        if e == args.workload:
+            continue
+        st = max(5, min(args.steps, 50))
+        q = time_workload(e, st, 3)
+        qt = q["ms"] / 1e3
+        qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
+        also[q["wl"].name] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
+                              "tflops": round(q["flops"] / qt / 1e12, 2),
+                              "frac_matrix_peak": round(q["flops"] / qt / 1e12 / qpk, 4),
+                              "frac_hbm": round(q["bytes"] / qt / 1e9 / PEAK_HBM_GBS, 4),
+                              "n_patches": q["n"], "steps": st}
+    cpu = None if args.no_cpu else cpu_baseline(args.workload)
+    line = {
+        "metric": METRIC, "value": round(r["n"] / t_s, 1), "unit": "patches/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms"], 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "n_patches": r["n"], "k": wl.k, "embed": wl.embed,
+                   "patch": wl.patch, "input": "%s %s" % (wl.kind, list(wl.input_shape)),
+                   "grid_thw": [list(g) for g in wl.grid[:1]] + (["x%d" % len(wl.grid)] if len(wl.grid) > 1 else []),
+                   "order": wl.order, "bias": wl.bias, "out_dtype": wl.out_dtype,
+                   "parallelism": "single GPU"},
+        "tflops": round(tflops, 3), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "eager_ms_per_step": round(r["eager_ms"], 6),
+        "timing": r["timing"],
+        "roofline": roof, "cpu_baseline": cpu, "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

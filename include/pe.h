@@ -1,0 +1,128 @@
+/*
+ * pe.h -- C ABI of the MI355X (gfx950) vision PatchEmbed library (libpe.so).
+ *
+ * The operation. The vision PatchEmbed of Qwen2/2.5/3-VL is a Conv3d with C = 3 input
+ * channels, E output channels and kernel = stride = (Tp, P, P), Tp = 2. Because the kernel
+ * covers a whole patch and stride equals kernel, each patch meets the kernel exactly once, so
+ * the convolution is a dot product of the flattened patch with each flattened filter
+ * ("Qwen2.5VL-Vision Encode-PatchEmbed", the bullet list on the convolution and its torch
+ * check): out[N, E] = patches[N, K] x W[E, K]^T (+ bias), K = C*Tp*P*P (1176 for P = 14,
+ * 1536 for P = 16). The pages' module interfaces are construct-once / forward-many: the candle
+ * struct's new() and forward() on that page, the Qwen3VLVisionPatchEmbed class and the vision
+ * model's forward(hidden_states, grid_thw) on "Optimize VLM PatchEmbed". This header mirrors
+ * them with pe_create / pe_forward / pe_destroy.
+ *
+ * All device pointers are HIP device memory on the device that was current at pe_create.
+ * Streams are hipStream_t passed as void* (NULL = the null stream). No call throws; every
+ * call returns a pe_status (or a count) and leaves a message for pe_last_error() on failure.
+ */
+#ifndef PE_H_
+#define PE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PE_OK = 0,
+    PE_ERR_INVALID_ARG = -1,  /* null pointer, bad enum value, negative count            */
+    PE_ERR_SHAPE = -2,        /* grid / frame counts inconsistent with the operation      */
+    PE_ERR_UNSUPPORTED = -3,  /* valid request outside what the kernels implement         */
+    PE_ERR_HIP = -4,          /* a HIP runtime call failed (message has hipGetErrorString) */
+    PE_ERR_OOM = -5           /* device allocation failed in pe_create                    */
+} pe_status;
+
+typedef enum { PE_F32 = 0, PE_BF16 = 1 } pe_dtype;
+
+/* Output row order for frames input.
+ *  RASTER:        rows follow the Conv3d output viewed as (-1, E), i.e. (t, h, w) raster
+ *                 order per item (the `.view(-1, embed_dim)` of the pages' PatchEmbed classes).
+ *  MERGE_WINDOW:  the rows of each m x m window of neighbouring patches are consecutive, as the
+ *                 PatchMerger concatenates them ("freechatgpt/mytransformer" section 3.2);
+ *                 windows follow the merged grid (t, h/m, w/m) in raster order (the vision
+ *                 position ids on the "Qwen2.5VL语言模型" page); inside a window the patches
+ *                 are in row-major (dh, dw) order (the pages leave this open; reading taken).
+ *  Pre-flattened patch rows keep their input order whatever this says. */
+typedef enum { PE_ORDER_RASTER = 0, PE_ORDER_MERGE_WINDOW = 1 } pe_order;
+
+/* What pe_forward receives.
+ *  PATCHES: rows x[N, K] row-major, each row flattened in (c, t, py, px) order, the
+ *           processor's pixel_values [N, 1176] (the `view(-1, 3, 2, 14, 14)` on the pages).
+ *  FRAMES:  raw frames. Item i is F_i frames of [C, h_i*P, w_i*P] row-major, items back to back
+ *           in one buffer. Temporal patch tp of item i reads frames min(tp*Tp + tt, F_i - 1),
+ *           tt < Tp: a single image frame fills both temporal slots ("patch详解" section 4.5
+ *           rounds 1/2 up to one temporal patch; repeating the frame is the reading taken). */
+typedef enum { PE_INPUT_PATCHES = 0, PE_INPUT_FRAMES = 1 } pe_input_kind;
+
+typedef struct {
+    int32_t in_channels;          /* C. Only 3 is supported.                                 */
+    int32_t temporal_patch_size;  /* Tp. Only 2 is supported.                                */
+    int32_t patch_size;           /* P. 14 or 16.                                            */
+    int32_t embed_dim;            /* E. Positive multiple of 16.                             */
+    int32_t spatial_merge_size;   /* m, used by PE_ORDER_MERGE_WINDOW (>= 1; the models: 2).  */
+    int32_t weight_dtype;         /* pe_dtype of weight and bias.                            */
+    int32_t out_dtype;            /* pe_dtype of the output.                                 */
+    int32_t out_order;            /* pe_order, applied to FRAMES input.                      */
+} pe_config;
+
+typedef struct pe_handle_s *pe_handle;
+
+/*
+ * pe_create -- validate the configuration and pre-pack the weight once.
+ *   cfg        configuration (read during the call only).
+ *   weight     device [E, C, Tp, P, P] row-major in cfg->weight_dtype: the checkpoint's
+ *              `visual.patch_embed.proj.weight` (the candle struct flattens and transposes it
+ *              once at load; this call re-lays it out once for the matrix cores instead).
+ *   bias       device [E] in cfg->weight_dtype, or NULL for no bias (Qwen2/2.5-VL have none,
+ *              the Qwen3-VL module has one: "Optimize VLM PatchEmbed").
+ *   hip_stream stream the packing runs on; the call synchronizes it before returning, so the
+ *              caller may free weight and bias afterwards.
+ *   out        receives the handle. The handle owns its packed copy (device memory).
+ * Returns PE_OK, PE_ERR_INVALID_ARG (null pointer, bad enum), PE_ERR_UNSUPPORTED (C != 3,
+ * Tp != 2, P not 14/16, E not a positive multiple of 16), PE_ERR_OOM or PE_ERR_HIP. On error
+ * *out is set to NULL and nothing is leaked.
+ */
+int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *hip_stream,
+              pe_handle *out);
+
+/*
+ * pe_forward -- out[N, E] = PatchEmbed(input), asynchronously on hip_stream.
+ *   h          handle from pe_create. Immutable: concurrent calls on different streams are safe.
+ *   input_kind pe_input_kind (see above).
+ *   input      device buffer (PATCHES: [N, K]; FRAMES: the items' frames back to back).
+ *   in_dtype   pe_dtype of the input; must equal the handle's weight dtype.
+ *   grid_thw   HOST int32 [n_items, 3]: per item (t, h, w) in patches; N = sum t*h*w.
+ *   frames     HOST int32 [n_items] frame counts F_i for FRAMES input, or NULL: then an item
+ *              with t = 1 is one image frame (F = 1) and an item with t > 1 has F = Tp*t.
+ *              Requires ceil(F_i / Tp) == t_i. Ignored for PATCHES.
+ *   n_items    number of items; 0 is a no-op that returns PE_OK.
+ *   out        device [N, E] in the handle's out dtype; rows of item i follow those of i-1.
+ * Arithmetic: products of the input and weight values accumulated in fp32, bias added in
+ * fp32, one round-to-nearest-even cast to the output dtype. Allocates nothing; does not take
+ * ownership of input or out, which must stay valid until the stream work completes.
+ * Returns PE_OK, PE_ERR_INVALID_ARG, PE_ERR_SHAPE (a non-positive t/h/w, F_i inconsistent
+ * with t_i, merge order with h or w not divisible by m, N >= 2^31), PE_ERR_UNSUPPORTED (dtype
+ * mismatch; one item's frames or one launch's patch rows beyond 4 GiB) or PE_ERR_HIP (launch
+ * failure). Validation happens before any launch.
+ */
+int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
+               const int32_t *grid_thw, const int32_t *frames, int32_t n_items, void *out,
+               void *hip_stream);
+
+/* N = sum over items of t*h*w ("freechatgpt/mytransformer" section 3.2: N = t*h*w), or a
+ * negative pe_status for a NULL grid, negative n_items or a non-positive entry. */
+int64_t pe_num_rows(const int32_t *grid_thw, int32_t n_items);
+
+/* Release the handle and its device memory (synchronizes the device first). NULL -> PE_OK. */
+int pe_destroy(pe_handle h);
+
+/* Message of the last failed call on this thread ("" if none). Valid until the next call. */
+const char *pe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PE_H_ */

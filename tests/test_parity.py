@@ -1,0 +1,278 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Tolerances (fixed by the workload statement, derived in the design doc):
+  * fp32 output from fp32 inputs: max |err| <= 5e-4 (unit-variance inputs);
+  * bf16 output: |err| <= 1e-3 + 1e-2 * |ref| elementwise;
+  * fp32 output from bf16 inputs: max |err| <= 5e-4;
+  * integer-valued inputs: fp32 output bit-exact, bf16 output == round-to-nearest-even(ref).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def pe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vlm_vision_patch_amd
+    return vlm_vision_patch_amd
+
+
+def say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def check(got, ref, out_dtype, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    err = np.abs(got - ref)
+    if out_dtype == torch.bfloat16:
+        bad = err > 1e-3 + 1e-2 * np.abs(ref)
+        assert not bad.any(), "%s: %d of %d outside 1e-3 + 1e-2|ref| (max err %.3g)" % (
+            what, bad.sum(), bad.size, err.max())
+    else:
+        assert err.max() <= 5e-4, "%s: max err %.3g > 5e-4" % (what, err.max())
+    return err.max()
+
+
+def run(pe, name, x, w, b, grid, frames=None, kind="frames", order="raster", out_dtype=None,
+        rows=None):
+    say("%s: kind=%s order=%s grid=%s frames=%s x=%s w=%s bias=%s out=%s" % (
+        name, kind, order, grid if len(grid) <= 4 else "%d items" % len(grid), frames if frames is None or len(frames) <= 4 else "...",
+        tuple(x.shape), tuple(w.shape), b is not None, out_dtype))
+    out_dtype = out_dtype or w.dtype
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV) if b is not None else None, order=order, out_dtype=out_dtype)
+    out = mod(x.to(DEV), grid, frames, kind=kind)
+    torch.cuda.synchronize()
+    if rows is not None:
+        got = out[torch.as_tensor(rows, device=DEV)].float().cpu().double().numpy()
+    else:
+        got = out.float().cpu().double().numpy()
+    ref = oracle.forward(x, w, b, grid=grid, frames=frames, kind=kind, order=order, rows=rows)
+    mod.close()
+    return got, ref, out_dtype
+
+
+# ---------------------------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------------------------
+
+def sampled_rows(n, seed, count):
+    """Rows the oracle computes one by one: first/last rows, every 256-row tile edge, items'
+    edges (5184-row images), plus a seeded random sample."""
+    rng = np.random.default_rng(seed)
+    edges = set([0, 1, n - 1, n - 2])
+    for step in (64, 256, 5184):
+        for e in range(step, n, step):
+            edges.update((e - 1, e))
+    picks = set(rng.choice(n, size=min(count, n), replace=False).tolist())
+    rows = sorted(r for r in edges | picks if 0 <= r < n)
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_workload_full(pe, idx):
+    wl = workloads.WORKLOADS[idx]
+    x, w, b = workloads.generate(wl)
+    got, ref, od = run(pe, wl.name, x, w, b, list(wl.grid), list(wl.frames) or None,
+                       kind=wl.kind, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype])
+    e = check(got, ref, od, wl.name)
+    print("%s: max err %.3g" % (wl.name, e), flush=True)
+
+
+def test_workload_5_sampled(pe):
+    wl = workloads.WORKLOADS[5]
+    x, w, b = workloads.generate(wl)
+    rows = sampled_rows(331776, seed=5, count=1500)
+    got, ref, od = run(pe, wl.name, x, w, b, list(wl.grid), list(wl.frames), kind=wl.kind,
+                       order=wl.order, out_dtype=torch.bfloat16, rows=rows)
+    e = check(got, ref, od, wl.name)
+    print("%s: %d sampled rows, max err %.3g" % (wl.name, len(rows), e), flush=True)
+
+
+def test_workload_5_raster_sampled(pe):
+    """The same batch in raster order: the order is a free choice of the caller."""
+    wl = workloads.WORKLOADS[5]
+    x, w, b = workloads.generate(wl)
+    rows = sampled_rows(331776, seed=6, count=500)
+    got, ref, od = run(pe, wl.name + "_raster", x, w, b, list(wl.grid), list(wl.frames),
+                       order="raster", out_dtype=torch.bfloat16, rows=rows)
+    check(got, ref, od, wl.name + " raster")
+
+
+# ---------------------------------------------------------------------------------------------
+# edge cases: ragged tails, several tiles, multi-item tables, orders, dtypes, bias, E tails
+# ---------------------------------------------------------------------------------------------
+
+def make(seed, shape, dtype, dist="normal", bound=1.0):
+    return workloads.random_tensor(shape, seed=seed, dtype=dtype, dist=dist, bound=bound)
+
+
+CASES = [
+    # name, P, E, items [(t,h,w,F)], order, in/w dtype, out dtype, bias
+    ("image_ragged_raster", 14, 1280, [(1, 6, 10, 1)], "raster", torch.bfloat16, torch.bfloat16, False),
+    ("image_ragged_merge", 14, 1280, [(1, 6, 10, 1)], "merge", torch.bfloat16, torch.bfloat16, True),
+    ("video_odd_frames", 14, 256, [(2, 4, 4, 3)], "merge", torch.bfloat16, torch.bfloat16, True),
+    ("mixed_items", 14, 512, [(1, 4, 6, 1), (3, 2, 4, 6), (1, 8, 2, 1), (2, 6, 6, 4)], "merge",
+     torch.bfloat16, torch.bfloat16, True),
+    ("mixed_items_raster", 14, 512, [(1, 3, 5, 1), (2, 3, 3, 3), (1, 7, 1, 1)], "raster",
+     torch.bfloat16, torch.bfloat16, False),
+    ("p16_e1152_tail", 16, 1152, [(1, 10, 12, 1), (1, 4, 4, 1)], "raster", torch.bfloat16, torch.bfloat16, True),
+    ("p16_video_merge", 16, 1024, [(2, 6, 8, 4)], "merge", torch.bfloat16, torch.bfloat16, True),
+    ("e16_minimum", 14, 16, [(1, 2, 2, 1)], "raster", torch.bfloat16, torch.bfloat16, True),
+    ("e48_odd_blocks", 14, 48, [(1, 4, 4, 1)], "merge", torch.bfloat16, torch.bfloat16, False),
+    ("bf16_in_f32_out", 14, 1280, [(1, 16, 20, 1)], "merge", torch.bfloat16, torch.float32, True),
+    ("f32_frames", 14, 640, [(1, 6, 8, 1), (2, 4, 2, 4)], "merge", torch.float32, torch.float32, True),
+    ("f32_p16_frames", 16, 320, [(1, 4, 6, 1)], "raster", torch.float32, torch.float32, False),
+    ("single_patch", 14, 1280, [(1, 1, 1, 1)], "raster", torch.bfloat16, torch.bfloat16, True),
+    ("large_merge_2k", 14, 1280, [(1, 40, 52, 1)], "merge", torch.bfloat16, torch.bfloat16, True),
+    ("tall_video_big_tiles", 14, 1280, [(8, 24, 24, 16)], "merge", torch.bfloat16, torch.bfloat16, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_frames_edge_cases(pe, case):
+    name, P, E, items, order, dt, od, bias = case
+    xs = [make(100 + i, (F, 3, h * P, w * P), dt) for i, (t, h, w, F) in enumerate(items)]
+    x = torch.cat([a.reshape(-1) for a in xs])
+    K = 3 * 2 * P * P
+    w = make(200, (E, 3, 2, P, P), dt, "uniform", 1 / math.sqrt(K))
+    b = make(201, (E,), dt, "uniform", 1 / math.sqrt(K)) if bias else None
+    grid = [[t, h, ww] for (t, h, ww, F) in items]
+    frames = [F for (*_, F) in items]
+    got, ref, _ = run(pe, name, x, w, b, grid, frames, order=order, out_dtype=od)
+    check(got, ref, od, name)
+
+
+@pytest.mark.parametrize("P,N,dt,od", [(14, 1, torch.bfloat16, torch.bfloat16),
+                                       (14, 333, torch.bfloat16, torch.bfloat16),
+                                       (16, 777, torch.bfloat16, torch.float32),
+                                       (14, 300, torch.float32, torch.float32),
+                                       (16, 65, torch.float32, torch.float32),
+                                       (14, 20000, torch.bfloat16, torch.bfloat16)])
+def test_patch_rows(pe, P, N, dt, od):
+    K = 3 * 2 * P * P
+    x = make(300 + N, (N, K), dt)
+    w = make(301, (1280, 3, 2, P, P), dt, "uniform", 1 / math.sqrt(K))
+    b = make(302, (1280,), dt, "uniform", 1 / math.sqrt(K))
+    rows = None if N <= 4000 else sampled_rows(N, 7, 500)
+    got, ref, _ = run(pe, "patches_P%d_N%d" % (P, N), x, w, b, [[1, 1, N]], kind="patches",
+                      out_dtype=od, rows=rows)
+    check(got, ref, od, "patches")
+
+
+def test_many_items_split_launches(pe):
+    """More items than one launch's item table holds: the library splits the launches."""
+    P, E = 14, 256
+    items = [(1, 2, 2 + 2 * (i % 3), 1) for i in range(150)]
+    xs = [make(400 + i, (F, 3, h * P, w * P), torch.bfloat16) for i, (t, h, w, F) in enumerate(items)]
+    x = torch.cat([a.reshape(-1) for a in xs])
+    w = make(401, (E, 3, 2, P, P), torch.bfloat16, "uniform", 0.03)
+    grid = [[t, h, ww] for (t, h, ww, F) in items]
+    got, ref, od = run(pe, "150_items", x, w, None, grid, [1] * 150, order="merge")
+    check(got, ref, od, "150 items")
+
+
+# ---------------------------------------------------------------------------------------------
+# integer inputs: exact results (the R1 == R2 check on the "Optimize VLM PatchEmbed" page)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P,od", [(16, torch.float32), (14, torch.float32), (14, torch.bfloat16)])
+def test_integer_inputs_exact(pe, P, od):
+    N = 123
+    K = 3 * 2 * P * P
+    x = workloads.random_tensor((N, K), seed=120, dist="int", low=0, high=3).to(torch.bfloat16)
+    w = workloads.random_tensor((1024, 3, 2, P, P), seed=121, dist="int", low=-2, high=3).to(torch.bfloat16)
+    b = workloads.random_tensor((1024,), seed=122, dist="int", low=-5, high=6).to(torch.bfloat16)
+    got, ref, _ = run(pe, "integers_P%d" % P, x, w, b, [[1, 1, N]], kind="patches", out_dtype=od)
+    assert np.abs(ref).max() < 2 ** 24
+    if od == torch.float32:
+        assert np.array_equal(got, ref)
+    else:
+        want = torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(got, want)
+
+
+def test_integer_frames_exact_merge_order(pe):
+    """Integer frames with a per-patch code make any row-order or gather mistake an exact miss."""
+    P, t, h, w, F = 14, 2, 4, 6, 4
+    x = workloads.random_tensor((F, 3, h * P, w * P), seed=130, dist="int", low=0, high=3).to(torch.bfloat16)
+    wt = workloads.random_tensor((64, 3, 2, P, P), seed=131, dist="int", low=-2, high=3).to(torch.bfloat16)
+    got, ref, _ = run(pe, "integer_frames_merge", x, wt, None, [[t, h, w]], [F], order="merge",
+                      out_dtype=torch.float32)
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# empty input and error paths (validated before any launch)
+# ---------------------------------------------------------------------------------------------
+
+def test_empty_batch(pe):
+    say("empty batch")
+    w = make(500, (64, 3, 2, 14, 14), torch.bfloat16).to(DEV)
+    mod = pe.PatchEmbed(w, order="merge")
+    out = mod(torch.empty(0, dtype=torch.bfloat16, device=DEV), [])
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 64)
+    assert pe.lib.pe_forward(mod._h, 1, 0x1000, 1, None, None, 0, 0x2000, None) == pe.PE_OK
+
+
+def test_forward_error_paths(pe):
+    import ctypes
+    say("error paths")
+    w = make(501, (64, 3, 2, 14, 14), torch.bfloat16).to(DEV)
+    mod = pe.PatchEmbed(w, order="merge")
+    h = mod._h
+    g = lambda *v: (ctypes.c_int32 * len(v))(*v)
+    X, O = 0x1000, 0x2000   # never dereferenced: every call below fails validation first
+    assert pe.lib.pe_forward(h, 1, X, 0, g(1, 2, 2), None, 1, O, None) == pe.PE_ERR_UNSUPPORTED  # dtype
+    assert pe.lib.pe_forward(h, 1, X, 1, g(1, 2, 3), None, 1, O, None) == pe.PE_ERR_SHAPE        # odd w
+    assert pe.lib.pe_forward(h, 1, X, 1, g(1, 2, 2), g(3), 1, O, None) == pe.PE_ERR_SHAPE        # F vs t
+    assert pe.lib.pe_forward(h, 1, X, 1, g(1, -2, 2), None, 1, O, None) == pe.PE_ERR_SHAPE
+    assert pe.lib.pe_forward(h, 7, X, 1, g(1, 2, 2), None, 1, O, None) == pe.PE_ERR_INVALID_ARG
+    assert pe.lib.pe_forward(h, 1, None, 1, g(1, 2, 2), None, 1, O, None) == pe.PE_ERR_INVALID_ARG
+    assert pe.lib.pe_forward(h, 1, X, 1, g(1, 2, 2), None, -1, O, None) == pe.PE_ERR_INVALID_ARG
+    # one item of frames beyond the 4 GiB launch range
+    assert pe.lib.pe_forward(h, 1, X, 1, g(1, 2000, 2000), g(1), 1, O, None) == pe.PE_ERR_UNSUPPORTED
+    assert "4 GiB" in pe.last_error()
+    with pytest.raises(pe.PEError):
+        mod(torch.zeros(10, dtype=torch.bfloat16, device=DEV), [[1, 2, 2]])   # wrong input size
+    mod.close()
+
+
+def test_graph_replays_match_eager(pe):
+    """The benchmark replays captured launches: every replay must equal the eager result, with
+    eager work and synchronisations between replays."""
+    wl = workloads.WORKLOADS[2]
+    x, w, b = workloads.generate(wl)
+    say("graph replay of %s" % wl.name)
+    mod = pe.PatchEmbed(w.to(DEV), None, order=wl.order)
+    xd = x.to(DEV)
+    eager = mod(xd, list(wl.grid), list(wl.frames))
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(3):
+            mod(xd, list(wl.grid), list(wl.frames), out=out)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "replay %d differs" % rep
+        other = mod(xd, list(wl.grid), list(wl.frames))     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+    mod.close()

@@ -1,0 +1,198 @@
+"""MI355X (gfx950) vision PatchEmbed: Python binding of libpe.so (include/pe.h).
+
+The binding only marshals arguments; every step of the operation runs in the library's HIP
+kernels. PyTorch supplies device memory and the current stream. There is no fallback: if the
+library is not built, importing this package raises.
+
+    pe = PatchEmbed(weight, bias, order="merge", out_dtype=torch.bfloat16)
+    out = pe(frames, grid_thw=[[1, 16, 64]])              # raw frames
+    out = pe(pixel_values, grid_thw=[[1, 16, 64]], kind="patches")
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpe.so")
+
+PE_OK, PE_ERR_INVALID_ARG, PE_ERR_SHAPE, PE_ERR_UNSUPPORTED, PE_ERR_HIP, PE_ERR_OOM = 0, -1, -2, -3, -4, -5
+PE_F32, PE_BF16 = 0, 1
+PE_ORDER_RASTER, PE_ORDER_MERGE_WINDOW = 0, 1
+PE_INPUT_PATCHES, PE_INPUT_FRAMES = 0, 1
+
+# every symbol include/pe.h declares
+EXPORTS = ("pe_create", "pe_forward", "pe_num_rows", "pe_destroy", "pe_last_error")
+
+
+class PEError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+class pe_config(ctypes.Structure):
+    _fields_ = [("in_channels", ctypes.c_int32), ("temporal_patch_size", ctypes.c_int32),
+                ("patch_size", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
+                ("spatial_merge_size", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("out_order", ctypes.c_int32)]
+
+
+def _load():
+    # Load torch's HIP runtime first: libpe.so then binds to it (same soname) instead of pulling
+    # a second HIP/HSA runtime from /opt/rocm into the process.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libpe.so is not built (%s); run `python __graft_entry__.py build` or "
+                          "`python vlm_vision_patch_amd/build.py`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.pe_create.restype = ctypes.c_int
+    lib.pe_create.argtypes = [ctypes.POINTER(pe_config), vp, vp, vp, ctypes.POINTER(vp)]
+    lib.pe_forward.restype = ctypes.c_int
+    lib.pe_forward.argtypes = [vp, i32, vp, i32, pi32, pi32, i32, vp, vp]
+    lib.pe_num_rows.restype = i64
+    lib.pe_num_rows.argtypes = [pi32, i32]
+    lib.pe_destroy.restype = ctypes.c_int
+    lib.pe_destroy.argtypes = [vp]
+    lib.pe_last_error.restype = ctypes.c_char_p
+    lib.pe_last_error.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.pe_last_error().decode("utf-8", "replace")
+
+
+def _check(rc):
+    if rc != PE_OK:
+        raise PEError(rc, last_error())
+    return rc
+
+
+def _i32_array(values):
+    flat = [int(v) for row in values for v in (row if hasattr(row, "__len__") else [row])]
+    return (ctypes.c_int32 * max(1, len(flat)))(*flat), len(flat)
+
+
+# ---- raw C-ABI calls with the header's names (plain integers / addresses) -------------------
+
+def pe_create(cfg: pe_config, weight_ptr: int, bias_ptr: int | None, stream: int | None) -> int:
+    h = ctypes.c_void_p()
+    _check(lib.pe_create(ctypes.byref(cfg), weight_ptr, bias_ptr, stream, ctypes.byref(h)))
+    return h.value
+
+
+def pe_forward(handle: int, input_kind: int, input_ptr: int, in_dtype: int, grid_thw, frames,
+               out_ptr: int, stream: int | None) -> None:
+    g, n = _i32_array(grid_thw)
+    f = _i32_array(frames)[0] if frames is not None else None
+    _check(lib.pe_forward(handle, input_kind, input_ptr, in_dtype, g, f, n // 3, out_ptr, stream))
+
+
+def pe_num_rows(grid_thw) -> int:
+    g, n = _i32_array(grid_thw)
+    rc = lib.pe_num_rows(g, n // 3)
+    if rc < 0:
+        raise PEError(int(rc), last_error())
+    return int(rc)
+
+
+def pe_destroy(handle: int) -> None:
+    _check(lib.pe_destroy(handle))
+
+
+# ---- torch-facing wrapper ------------------------------------------------------------------
+
+def _dtype_code(dt):
+    import torch
+    if dt == torch.bfloat16:
+        return PE_BF16
+    if dt == torch.float32:
+        return PE_F32
+    raise PEError(PE_ERR_UNSUPPORTED, "dtype %s: only bfloat16 and float32" % dt)
+
+
+class PatchEmbed:
+    """Conv3d(3, E, (2, P, P), stride (2, P, P)) PatchEmbed on the current CUDA/HIP device.
+
+    weight  [E, 3, 2, P, P] bf16 or fp32 CUDA tensor (packed once at construction)
+    bias    [E] same dtype, or None
+    order   "merge" (2x2 merge-window rows) or "raster" (Conv3d view order) for frames input
+    """
+
+    def __init__(self, weight, bias=None, *, order: str = "raster", out_dtype=None,
+                 spatial_merge_size: int = 2):
+        import torch
+        if weight.dim() != 5 or weight.shape[3] != weight.shape[4]:
+            raise PEError(PE_ERR_INVALID_ARG, "weight must be [E, C, Tp, P, P]")
+        if not weight.is_cuda:
+            raise PEError(PE_ERR_INVALID_ARG, "weight must be a device tensor")
+        E, C, Tp, P, _ = weight.shape
+        self.device = weight.device
+        self.weight_dtype = weight.dtype
+        self.out_dtype = out_dtype if out_dtype is not None else weight.dtype
+        self.embed_dim, self.patch_size = int(E), int(P)
+        self.k = int(C * Tp * P * P)
+        self.order = order
+        cfg = pe_config(int(C), int(Tp), int(P), int(E), int(spatial_merge_size),
+                        _dtype_code(weight.dtype), _dtype_code(self.out_dtype),
+                        PE_ORDER_MERGE_WINDOW if order == "merge" else PE_ORDER_RASTER)
+        w = weight.contiguous()
+        b = bias.contiguous() if bias is not None else None
+        if b is not None and (b.dtype != weight.dtype or b.numel() != E):
+            raise PEError(PE_ERR_INVALID_ARG, "bias must be [E] in the weight dtype")
+        with torch.cuda.device(self.device):
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+            self._h = pe_create(cfg, w.data_ptr(), b.data_ptr() if b is not None else None, stream)
+
+    def __call__(self, x, grid_thw, frames=None, *, kind: str = "frames", out=None, stream=None):
+        import torch
+        grid = [[int(v) for v in row] for row in (grid_thw.tolist() if hasattr(grid_thw, "tolist") else grid_thw)]
+        fr = None
+        if frames is not None:
+            fr = [int(v) for v in (frames.tolist() if hasattr(frames, "tolist") else frames)]
+        n = pe_num_rows(grid) if grid else 0
+        if out is None:
+            out = torch.empty((n, self.embed_dim), dtype=self.out_dtype, device=self.device)
+        elif tuple(out.shape) != (n, self.embed_dim) or out.dtype != self.out_dtype or not out.is_contiguous():
+            raise PEError(PE_ERR_INVALID_ARG, "out must be a contiguous [%d, %d] %s tensor"
+                          % (n, self.embed_dim, self.out_dtype))
+        if n == 0:
+            return out
+        if not x.is_cuda or x.device != self.device:
+            raise PEError(PE_ERR_INVALID_ARG, "input must be on %s" % self.device)
+        need = self.input_elements(grid, fr, kind)
+        if x.numel() != need:
+            raise PEError(PE_ERR_SHAPE, "input has %d elements; the grid needs %d" % (x.numel(), need))
+        x = x.contiguous()
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        pe_forward(self._h, PE_INPUT_PATCHES if kind == "patches" else PE_INPUT_FRAMES, x.data_ptr(),
+                   _dtype_code(x.dtype), grid, fr, out.data_ptr(), stream)
+        return out
+
+    def input_elements(self, grid, frames=None, kind="frames") -> int:
+        """Elements the library will read for this grid (the C ABI trusts the caller on this)."""
+        if kind == "patches":
+            return pe_num_rows(grid) * self.k
+        P, total = self.patch_size, 0
+        for i, (t, h, w) in enumerate(grid):
+            f = frames[i] if frames is not None else (1 if t == 1 else 2 * t)
+            total += f * 3 * (h * P) * (w * P)
+        return total
+
+    def close(self):
+        if getattr(self, "_h", None):
+            pe_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

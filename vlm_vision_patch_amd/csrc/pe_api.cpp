@@ -1,0 +1,274 @@
+// pe_api.cpp -- the C ABI of include/pe.h: validation, the weight pre-pack at create, and the
+// launch plan of pe_forward (item tables, launch splitting). No allocation after pe_create.
+#include "pe.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include <string>
+#include <vector>
+
+#include "pe_internal.h"
+
+struct pe_handle_s {
+    pe_config cfg;
+    int device;
+    int steps;
+    void *wpk;      // packed weight, steps * E * 64 bytes
+    float *bias32;  // fp32 bias or null
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(PE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int esize(int32_t dt) { return dt == PE_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dt) { return dt == PE_F32 || dt == PE_BF16; }
+
+// Keeps the caller's current device; switches to the handle's device for the call.
+struct DeviceGuard {
+    int prev = -1;
+    bool switched = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            switched = err == hipSuccess;
+        }
+    }
+    ~DeviceGuard() {
+        if (switched) (void)hipSetDevice(prev);
+    }
+};
+
+constexpr uint64_t kMaxLaunchBytes = 0xFFFFFFF0ull;  // buffer range of one launch (32-bit offsets)
+
+}  // namespace
+
+extern "C" {
+
+const char *pe_last_error(void) { return g_err.c_str(); }
+
+int64_t pe_num_rows(const int32_t *grid_thw, int32_t n_items) {
+    if (n_items < 0) return fail(PE_ERR_INVALID_ARG, "n_items must be >= 0 (got %d)", n_items);
+    if (n_items == 0) return 0;
+    if (!grid_thw) return fail(PE_ERR_INVALID_ARG, "grid_thw is NULL");
+    int64_t n = 0;
+    for (int i = 0; i < n_items; ++i) {
+        const int32_t t = grid_thw[3 * i], h = grid_thw[3 * i + 1], w = grid_thw[3 * i + 2];
+        if (t <= 0 || h <= 0 || w <= 0)
+            return fail(PE_ERR_SHAPE, "item %d: grid (%d, %d, %d) has a non-positive entry", i, t, h, w);
+        n += (int64_t)t * h * w;
+    }
+    return n;
+}
+
+int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *hip_stream,
+              pe_handle *out) {
+    if (!out) return fail(PE_ERR_INVALID_ARG, "out (handle pointer) is NULL");
+    *out = nullptr;
+    if (!cfg) return fail(PE_ERR_INVALID_ARG, "cfg is NULL");
+    if (!weight) return fail(PE_ERR_INVALID_ARG, "weight is NULL");
+    if (!dtype_ok(cfg->weight_dtype) || !dtype_ok(cfg->out_dtype))
+        return fail(PE_ERR_INVALID_ARG, "bad dtype (weight %d, out %d)", cfg->weight_dtype, cfg->out_dtype);
+    if (cfg->out_order != PE_ORDER_RASTER && cfg->out_order != PE_ORDER_MERGE_WINDOW)
+        return fail(PE_ERR_INVALID_ARG, "bad out_order %d", cfg->out_order);
+    if (cfg->out_order == PE_ORDER_MERGE_WINDOW && cfg->spatial_merge_size < 1)
+        return fail(PE_ERR_INVALID_ARG, "spatial_merge_size must be >= 1 (got %d)", cfg->spatial_merge_size);
+    if (cfg->in_channels != pe::kC)
+        return fail(PE_ERR_UNSUPPORTED, "in_channels %d: only 3 is supported", cfg->in_channels);
+    if (cfg->temporal_patch_size != pe::kTp)
+        return fail(PE_ERR_UNSUPPORTED, "temporal_patch_size %d: only 2 is supported", cfg->temporal_patch_size);
+    if (!pe::patch_supported(cfg->patch_size))
+        return fail(PE_ERR_UNSUPPORTED, "patch_size %d: only 14 and 16 are supported", cfg->patch_size);
+    if (cfg->embed_dim <= 0 || cfg->embed_dim % 16 != 0)
+        return fail(PE_ERR_UNSUPPORTED, "embed_dim %d: must be a positive multiple of 16", cfg->embed_dim);
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const int wes = esize(cfg->weight_dtype);
+    const int steps = pe::num_steps(cfg->patch_size, wes);
+    const size_t wpk_bytes = (size_t)steps * cfg->embed_dim * 64;
+
+    pe_handle h = new (std::nothrow) pe_handle_s;
+    if (!h) return fail(PE_ERR_OOM, "host allocation failed");
+    h->cfg = *cfg;
+    h->device = dev;
+    h->steps = steps;
+    h->wpk = nullptr;
+    h->bias32 = nullptr;
+    e = hipMalloc(&h->wpk, wpk_bytes);
+    if (e != hipSuccess) {
+        delete h;
+        (void)hipGetLastError();
+        return fail(PE_ERR_OOM, "hipMalloc(%zu) for the packed weight: %s", wpk_bytes, hipGetErrorString(e));
+    }
+    if (bias) {
+        e = hipMalloc(reinterpret_cast<void **>(&h->bias32), sizeof(float) * cfg->embed_dim);
+        if (e != hipSuccess) {
+            (void)hipFree(h->wpk);
+            delete h;
+            (void)hipGetLastError();
+            return fail(PE_ERR_OOM, "hipMalloc for the bias: %s", hipGetErrorString(e));
+        }
+    }
+    e = pe::launch_pack(weight, wes, h->wpk, cfg->patch_size, cfg->embed_dim, st);
+    if (e == hipSuccess && bias) e = pe::launch_bias(bias, wes, h->bias32, cfg->embed_dim, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        int rc = hip_fail(e, "weight pre-pack");
+        (void)hipFree(h->wpk);
+        if (h->bias32) (void)hipFree(h->bias32);
+        delete h;
+        return rc;
+    }
+    *out = h;
+    g_err.clear();
+    return PE_OK;
+}
+
+int pe_destroy(pe_handle h) {
+    if (!h) return PE_OK;
+    DeviceGuard dg(h->device);
+    hipError_t e1 = hipFree(h->wpk);
+    hipError_t e2 = h->bias32 ? hipFree(h->bias32) : hipSuccess;
+    delete h;
+    if (e1 != hipSuccess) return hip_fail(e1, "hipFree");
+    if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
+    return PE_OK;
+}
+
+int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
+               const int32_t *grid_thw, const int32_t *frames, int32_t n_items, void *out,
+               void *hip_stream) {
+    if (!h) return fail(PE_ERR_INVALID_ARG, "handle is NULL");
+    if (n_items < 0) return fail(PE_ERR_INVALID_ARG, "n_items must be >= 0 (got %d)", n_items);
+    if (n_items == 0) return PE_OK;
+    if (!grid_thw) return fail(PE_ERR_INVALID_ARG, "grid_thw is NULL");
+    if (!input) return fail(PE_ERR_INVALID_ARG, "input is NULL");
+    if (!out) return fail(PE_ERR_INVALID_ARG, "out is NULL");
+    if (input_kind != PE_INPUT_PATCHES && input_kind != PE_INPUT_FRAMES)
+        return fail(PE_ERR_INVALID_ARG, "bad input_kind %d", input_kind);
+    if (!dtype_ok(in_dtype)) return fail(PE_ERR_INVALID_ARG, "bad in_dtype %d", in_dtype);
+    const pe_config &cfg = h->cfg;
+    if (in_dtype != cfg.weight_dtype)
+        return fail(PE_ERR_UNSUPPORTED, "in_dtype %d differs from the weight dtype %d", in_dtype, cfg.weight_dtype);
+
+    const int P = cfg.patch_size, E = cfg.embed_dim, m = cfg.spatial_merge_size;
+    const int ies = esize(in_dtype), oes = esize(cfg.out_dtype);
+    const int64_t K = (int64_t)pe::kC * pe::kTp * P * P;
+    const bool merge = input_kind == PE_INPUT_FRAMES && cfg.out_order == PE_ORDER_MERGE_WINDOW;
+
+    // ---- validate every item before any launch
+    std::vector<int32_t> F(n_items);
+    std::vector<int64_t> row0(n_items + 1), elems(n_items);
+    int64_t N = 0;
+    for (int i = 0; i < n_items; ++i) {
+        const int32_t t = grid_thw[3 * i], hh = grid_thw[3 * i + 1], ww = grid_thw[3 * i + 2];
+        if (t <= 0 || hh <= 0 || ww <= 0)
+            return fail(PE_ERR_SHAPE, "item %d: grid (%d, %d, %d) has a non-positive entry", i, t, hh, ww);
+        if (input_kind == PE_INPUT_FRAMES) {
+            const int32_t f = frames ? frames[i] : (t == 1 ? 1 : pe::kTp * t);
+            if (f <= 0 || (f + pe::kTp - 1) / pe::kTp != t)
+                return fail(PE_ERR_SHAPE, "item %d: %d frames do not make t = %d temporal patches", i, f, t);
+            if (merge && (hh % m || ww % m))
+                return fail(PE_ERR_SHAPE, "item %d: grid %d x %d not divisible by merge size %d", i, hh, ww, m);
+            F[i] = f;
+            elems[i] = (int64_t)f * pe::kC * hh * P * (int64_t)ww * P;
+            if ((uint64_t)elems[i] * ies > kMaxLaunchBytes)
+                return fail(PE_ERR_UNSUPPORTED, "item %d: %lld bytes of frames exceed the 4 GiB launch range",
+                            i, (long long)(elems[i] * ies));
+        }
+        row0[i] = N;
+        N += (int64_t)t * hh * ww;
+    }
+    row0[n_items] = N;
+    if (N >= ((int64_t)1 << 31)) return fail(PE_ERR_SHAPE, "N = %lld rows: must be < 2^31", (long long)N);
+
+    DeviceGuard dg(h->device);
+    if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+
+    pe::FwdArgs a;
+    memset(&a, 0, sizeof a);
+    a.wpk = h->wpk;
+    a.bias = h->bias32;
+    a.E = E;
+    a.m = m;
+    a.order = merge ? 1 : 0;
+
+    if (input_kind == PE_INPUT_PATCHES) {
+        // patch rows: launches of at most kMaxLaunchBytes of input
+        const int64_t rows_per = (int64_t)(kMaxLaunchBytes / (uint64_t)(K * ies));
+        for (int64_t r = 0; r < N; r += rows_per) {
+            const int64_t nr = (N - r < rows_per) ? N - r : rows_per;
+            a.kind = 0;
+            a.in = static_cast<const char *>(input) + r * K * ies;
+            a.in_bytes = (uint32_t)(nr * K * ies);
+            a.out = static_cast<char *>(out) + r * E * oes;
+            a.n_rows = (int32_t)nr;
+            a.n_items = 0;
+            hipError_t e = pe::launch_forward(a, P, ies, oes, st);
+            if (e != hipSuccess) return hip_fail(e, "forward launch");
+        }
+        return PE_OK;
+    }
+
+    // frames: launches of at most kMaxItems items and kMaxLaunchBytes of input
+    int64_t x0 = 0;  // element offset of item i0
+    int i0 = 0;
+    while (i0 < n_items) {
+        int i1 = i0;
+        int64_t span = 0;
+        while (i1 < n_items && i1 - i0 < pe::kMaxItems &&
+               (uint64_t)(span + elems[i1]) * ies <= kMaxLaunchBytes) {
+            span += elems[i1];
+            ++i1;
+        }
+        a.kind = 1;
+        a.in = static_cast<const char *>(input) + x0 * ies;
+        a.in_bytes = (uint32_t)(span * ies);
+        a.out = static_cast<char *>(out) + row0[i0] * E * oes;
+        a.n_rows = (int32_t)(row0[i1] - row0[i0]);
+        a.n_items = i1 - i0;
+        int64_t off = 0;
+        for (int i = i0; i < i1; ++i) {
+            pe::Item &it = a.items[i - i0];
+            it.row0 = (int32_t)(row0[i] - row0[i0]);
+            it.t = grid_thw[3 * i];
+            it.h = grid_thw[3 * i + 1];
+            it.w = grid_thw[3 * i + 2];
+            it.F = F[i];
+            it.x_off = (uint32_t)off;
+            off += elems[i];
+        }
+        hipError_t e = pe::launch_forward(a, P, ies, oes, st);
+        if (e != hipSuccess) return hip_fail(e, "forward launch");
+        x0 += span;
+        i0 = i1;
+    }
+    return PE_OK;
+}
+
+}  // extern "C"
