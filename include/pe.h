@@ -60,7 +60,7 @@ typedef struct {
     int32_t in_channels;          /* C. Only 3 is supported.                                 */
     int32_t temporal_patch_size;  /* Tp. Only 2 is supported.                                */
     int32_t patch_size;           /* P. 14 or 16.                                            */
-    int32_t embed_dim;            /* E. Positive multiple of 16.                             */
+    int32_t embed_dim;            /* E. Positive multiple of 16, at most 65536.              */
     int32_t spatial_merge_size;   /* m, used by PE_ORDER_MERGE_WINDOW (>= 1; the models: 2).  */
     int32_t weight_dtype;         /* pe_dtype of weight and bias.                            */
     int32_t out_dtype;            /* pe_dtype of the output.                                 */
@@ -81,7 +81,8 @@ typedef struct pe_handle_s *pe_handle;
  *              caller may free weight and bias afterwards.
  *   out        receives the handle. The handle owns its packed copy (device memory).
  * Returns PE_OK, PE_ERR_INVALID_ARG (null pointer, bad enum), PE_ERR_UNSUPPORTED (C != 3,
- * Tp != 2, P not 14/16, E not a positive multiple of 16), PE_ERR_OOM or PE_ERR_HIP. On error
+ * Tp != 2, P not 14/16, E not a positive multiple of 16 or above 65536), PE_ERR_OOM or
+ * PE_ERR_HIP. On error
  * *out is set to NULL and nothing is leaked.
  */
 int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *hip_stream,
@@ -99,9 +100,10 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
  *              Requires ceil(F_i / Tp) == t_i. Ignored for PATCHES.
  *   n_items    number of items; 0 is a no-op that returns PE_OK.
  *   out        device [N, E] in the handle's out dtype; rows of item i follow those of i-1.
- * Arithmetic: products of the input and weight values accumulated in fp32, bias added in
- * fp32, one round-to-nearest-even cast to the output dtype. Allocates nothing; does not take
- * ownership of input or out, which must stay valid until the stream work completes.
+ * Arithmetic: products of the input and weight values accumulated in fp32 together with the
+ * fp32 bias, one round-to-nearest-even cast to the output dtype. Allocates nothing; does not
+ * take ownership of input or out, which must stay valid until the stream work completes. One
+ * kernel launch covers up to 64 consecutive items of one frame size (h, w).
  * Returns PE_OK, PE_ERR_INVALID_ARG, PE_ERR_SHAPE (a non-positive t/h/w, F_i inconsistent
  * with t_i, merge order with h or w not divisible by m, N >= 2^31), PE_ERR_UNSUPPORTED (dtype
  * mismatch; one item's frames or one launch's patch rows beyond 4 GiB) or PE_ERR_HIP (launch

@@ -36,10 +36,37 @@ static int check(int P, int esz) {
     return 0;
 }
 
+// The temporal-split map of the bf16 32x32 kernel: fragment (s, g = 2j + tt) covers unique
+// fragment uf = 2s + j of temporal slot tt; every element of each slot exactly once.
+static int check_tt(int P) {
+    using namespace pe;
+    const int rows = kC * P, S = tt_steps(P);
+    std::vector<int> hits(rows * P, 0);
+    int pads = 0;
+    for (int uf = 0; uf < 2 * S; ++uf) {
+        const UFrag f = tt_frag(P, uf);
+        for (int j = 0; j < 8; ++j) {
+            int u = f.u1, x = f.x1 + j;
+            if (f.kind == kUfSplit62 && j >= 6) { u = f.u2; x = f.x2 + j - 6; }
+            if (f.kind == kUfTail4 && j >= 4) { ++pads; continue; }
+            if (u < 0 || u >= rows || x < 0 || x >= P) { printf("tt map out of row\n"); return 1; }
+            hits[u * P + x]++;
+        }
+        if ((f.x1 * 2) % 4 || (f.kind == kUfSplit62 && (f.x2 * 2) % 4)) { printf("misaligned\n"); return 1; }
+        if (f.kind != kUfFull && f.x1 + (f.kind == kUfSplit62 ? 6 : 4) > P) { printf("piece 1 past row\n"); return 1; }
+    }
+    for (int i = 0; i < rows * P; ++i)
+        if (hits[i] != 1) { printf("tt map P%d element %d hit %d times\n", P, i, hits[i]); return 1; }
+    printf("tt map P%d: %d steps, %d pad elements per temporal slot\n", P, S, pads);
+    return pads == 2 * S * 8 - rows * P ? 0 : 1;
+}
+
 int main() {
     int bad = 0;
     for (int P : {14, 16})
         for (int esz : {2, 4}) bad |= check(P, esz);
+    for (int P : {14, 16}) bad |= check_tt(P);
+    if (pe::tt_steps(14) != 37 || pe::tt_steps(16) != 48) { printf("tt step counts\n"); bad = 1; }
     if (pe::num_steps(14, 2) != 37 || pe::num_steps(16, 2) != 48) { printf("step counts\n"); bad = 1; }
     if (!bad) printf("OK\n");
     return bad;

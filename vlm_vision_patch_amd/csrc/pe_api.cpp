@@ -17,7 +17,7 @@ struct pe_handle_s {
     pe_config cfg;
     int device;
     int steps;
-    void *wpk;      // packed weight, steps * E * 64 bytes
+    void *wpk;      // packed weight, steps * packed_cols(E) * 64 bytes
     float *bias32;  // fp32 bias or null
 };
 
@@ -100,16 +100,17 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
         return fail(PE_ERR_UNSUPPORTED, "temporal_patch_size %d: only 2 is supported", cfg->temporal_patch_size);
     if (!pe::patch_supported(cfg->patch_size))
         return fail(PE_ERR_UNSUPPORTED, "patch_size %d: only 14 and 16 are supported", cfg->patch_size);
-    if (cfg->embed_dim <= 0 || cfg->embed_dim % 16 != 0)
-        return fail(PE_ERR_UNSUPPORTED, "embed_dim %d: must be a positive multiple of 16", cfg->embed_dim);
+    if (cfg->embed_dim <= 0 || cfg->embed_dim % 16 != 0 || cfg->embed_dim > 65536)
+        return fail(PE_ERR_UNSUPPORTED, "embed_dim %d: must be a positive multiple of 16, at most 65536",
+                    cfg->embed_dim);
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const int wes = esize(cfg->weight_dtype);
-    const int steps = pe::num_steps(cfg->patch_size, wes);
-    const size_t wpk_bytes = (size_t)steps * cfg->embed_dim * 64;
+    const int steps = pe::packed_steps(cfg->patch_size, wes);
+    const size_t wpk_bytes = (size_t)steps * pe::packed_cols(cfg->embed_dim, wes) * 64;
 
     pe_handle h = new (std::nothrow) pe_handle_s;
     if (!h) return fail(PE_ERR_OOM, "host allocation failed");
@@ -224,6 +225,8 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         for (int64_t r = 0; r < N; r += rows_per) {
             const int64_t nr = (N - r < rows_per) ? N - r : rows_per;
             a.kind = 0;
+            a.plane = (uint32_t)(pe::kTp * P * P);  // a row is [C][Tp][P][P]
+            a.rstr = (uint32_t)P;
             a.in = static_cast<const char *>(input) + r * K * ies;
             a.in_bytes = (uint32_t)(nr * K * ies);
             a.out = static_cast<char *>(out) + r * E * oes;
@@ -235,18 +238,22 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         return PE_OK;
     }
 
-    // frames: launches of at most kMaxItems items and kMaxLaunchBytes of input
+    // frames: launches of at most kMaxItems consecutive items of one frame geometry (h, w) and
+    // at most kMaxLaunchBytes of input
     int64_t x0 = 0;  // element offset of item i0
     int i0 = 0;
     while (i0 < n_items) {
         int i1 = i0;
         int64_t span = 0;
         while (i1 < n_items && i1 - i0 < pe::kMaxItems &&
+               grid_thw[3 * i1 + 1] == grid_thw[3 * i0 + 1] && grid_thw[3 * i1 + 2] == grid_thw[3 * i0 + 2] &&
                (uint64_t)(span + elems[i1]) * ies <= kMaxLaunchBytes) {
             span += elems[i1];
             ++i1;
         }
         a.kind = 1;
+        a.rstr = (uint32_t)grid_thw[3 * i0 + 2] * (uint32_t)P;
+        a.plane = (uint32_t)grid_thw[3 * i0 + 1] * (uint32_t)P * a.rstr;
         a.in = static_cast<const char *>(input) + x0 * ies;
         a.in_bytes = (uint32_t)(span * ies);
         a.out = static_cast<char *>(out) + row0[i0] * E * oes;

@@ -33,7 +33,7 @@ struct FwdArgs {
     int32_t m;           // merge size
     int32_t n_items;
     int32_t tiles_m, tiles_n;
-    int32_t pad_;
+    uint32_t plane, rstr;  // channel and pixel-row strides (elements), the same for every row
     Item items[kMaxItems];
 };
 
@@ -61,6 +61,13 @@ __host__ __device__ constexpr int split_frags(int P, int esz) {
 }
 __host__ __device__ constexpr int num_steps(int P, int esz) {
     return full_steps(P, esz) + (split_frags(P, esz) + 3) / 4;
+}
+// Packed weight layout: [step][column block of NB][lane group g][NB columns][16 bytes], NB = 32
+// for bf16 (32x32 matrix-core blocks) and 16 for fp32 (16x16 blocks); E is padded with zero
+// columns up to a multiple of NB.
+__host__ __device__ constexpr int pack_block(int esz) { return esz == 2 ? 32 : 16; }
+__host__ __device__ constexpr int packed_cols(int E, int esz) {
+    return (E + pack_block(esz) - 1) / pack_block(esz) * pack_block(esz);
 }
 // P values the fragment map covers: P % 8 == 0 (all whole fragments) or P == 14.
 __host__ __device__ constexpr bool patch_supported(int P) { return P == 14 || P == 16; }
@@ -93,6 +100,60 @@ __host__ __device__ inline Piece frag_piece(int P, int esz, int s, int g) {
         p.x2 = per * epf;
     }
     return p;
+}
+
+// bf16 fragment map of the 32x32x16 kernel. A k-step holds four 8-element fragments
+// g = 2j + h: h is the temporal slot tt (the two lane halves of a 32x32x16 product read the two
+// frames of a temporal patch, or the same frame twice for an image), j picks one of the step's
+// two "unique" fragments uf = 2s + j over the C*P pixel rows u = c*P + py of one temporal slot.
+//   P % 8 == 0: row u = uf / (P/8), px 8*(uf % (P/8)) .. +7 (one 16-byte load).
+//   P == 14:    uf < 42: row uf, px 0..7;
+//               42 <= uf < 72: rows a..d = 4q..4q+3, q = (uf-42)/3, i = (uf-42)%3:
+//                              row a+i px 8..13 (12 bytes) + row d px 8+2i..9+2i (4 bytes);
+//               uf == 72:      row 40 px 8..13 + row 41 px 8..9;
+//               uf == 73:      row 41 px 10..13 (8 bytes) + 4 zero elements.
+// 37 steps for P = 14 (1184 = 1176 + 8 zero k), 48 for P = 16.
+enum UfKind { kUfFull = 0, kUfSplit62 = 1, kUfTail4 = 2 };
+struct UFrag {
+    int kind;
+    int u1, x1;  // first piece: pixel row within the temporal slot, first px
+    int u2, x2;  // second piece (kUfSplit62)
+};
+__host__ __device__ constexpr int tt_steps(int P) {
+    return P % 8 == 0 ? kC * P * (P / 8) / 2 : (P == 14 ? 37 : 0);
+}
+__host__ __device__ constexpr UFrag tt_frag(int P, int uf) {
+    UFrag f{kUfFull, 0, 0, 0, 0};
+    if (P % 8 == 0) {
+        f.u1 = uf / (P / 8);
+        f.x1 = 8 * (uf % (P / 8));
+        return f;
+    }
+    if (uf < kC * P) {            // 42 whole fragments
+        f.u1 = uf;
+        return f;
+    }
+    if (uf < 72) {
+        const int q = (uf - 42) / 3, i = (uf - 42) % 3;
+        f.kind = kUfSplit62;
+        f.u1 = 4 * q + i; f.x1 = 8;
+        f.u2 = 4 * q + 3; f.x2 = 8 + 2 * i;
+        return f;
+    }
+    if (uf == 72) {
+        f.kind = kUfSplit62;
+        f.u1 = 40; f.x1 = 8;
+        f.u2 = 41; f.x2 = 8;
+        return f;
+    }
+    f.kind = kUfTail4;
+    f.u1 = 41; f.x1 = 10;
+    return f;
+}
+
+// k-steps of the packed weight: the temporal-split map for bf16, frag_piece's map for fp32
+__host__ __device__ constexpr int packed_steps(int P, int esz) {
+    return esz == 2 ? tt_steps(P) : num_steps(P, esz);
 }
 
 // Launchers (pe_kernels.hip). Return the launch status.

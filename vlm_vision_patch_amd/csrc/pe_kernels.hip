@@ -4,7 +4,7 @@
 // a Conv3d whose kernel equals its stride meets each patch once, so it is a matrix product
 //   out[r, e] = sum_k A[r, k] * W[e, k] (+ b[e]),  K = C*Tp*P*P,
 // where A[r, :] is the patch behind output row r, flattened. Nothing materialises A: the
-// forward kernel reads each patch's pixels straight from the frames (or patch rows) into the
+// forward kernels read each patch's pixels straight from the frames (or patch rows) into the
 // registers that feed the matrix cores.
 //
 // K order. Any permutation of k applied to both A and W leaves the sum unchanged, so the
@@ -13,21 +13,28 @@
 // (px 0..7, one 16-byte load) and a 6-element rest; the rests of rows a, b, c, d form three
 // fragments (a[8:14] + d[8:10]), (b[8:14] + d[10:12]), (c[8:14] + d[12:14]), each a 12-byte
 // and a 4-byte load. 84 rows give 84 + 63 fragments; one zero fragment pads them to 37
-// k-steps of 32 (1184 = 1176 + 8). For P = 16 every row is two whole fragments (48 steps).
-// fp32 uses 4-element fragments the same way (P = 14: 3 whole + pairs of 2-element rests).
-// The weight is packed once in exactly this order (pe_pack_kernel).
+// k-steps of four fragments (1184 = 1176 + 8). For P = 16 every row is two whole fragments
+// (48 steps). fp32 uses 4-element fragments the same way (P = 14: 3 whole + pairs of
+// 2-element rests). The weight is packed once in exactly this order (pe_pack_kernel).
 //
-// Forward kernel layout. A workgroup computes a BM x BN output tile with WM x WN waves; each
-// wave owns TM x TN blocks of 16 x 16. The wave loads its own A fragments from global memory
-// (raw buffer loads: 32-bit offsets, reads past the input range return 0), so A never passes
-// through LDS. The packed weight for one k-step and the tile's BN columns is one contiguous
-// BN*64-byte run; it is staged through a double-buffered LDS stage and read back as one
-// conflict-free 16-byte ds_read per lane and 16-column block. Matrix core:
-// v_mfma_f32_16x16x32_bf16 (fp32 accumulate) or v_mfma_f32_16x16x4_f32.
+// bf16 kernel (pe_fwd32_kernel): v_mfma_f32_32x32x16_bf16, fp32 accumulate. (Measured on this
+// chip: the 32x32x16 form keeps the matrix pipe ~87% busy from a single wave per SIMD; the
+// 16x16x32 form reaches only ~54% from one wave.) A k-step of four fragments is two 32x32x16
+// products: lane l supplies row (or column) l % 32 and fragment g = 2j + l / 32 in sub-step j.
+// A workgroup computes a BM x BN tile with WM x WN waves, each wave TM x TN blocks of 32 x 32.
+// Each wave loads its own A fragments with raw buffer loads (32-bit offsets; reads past the
+// range return 0), so A never passes through LDS. The packed weight for one k-step and the
+// tile's columns is one contiguous run, staged in LDS (KS k-steps per buffer, two buffers) and
+// read as one conflict-free 1 KB ds_read_b128 per sub-step and 32-column block.
 //
-// Rows of the tile are output rows in output order; each lane maps its row back to the patch
+// fp32 kernel (pe_fwd16_kernel): the same structure with 16x16 blocks and v_mfma_f32_16x16x4_f32.
+//
+// Rows of a tile are output rows in output order; each lane maps its row back to the patch
 // (item, tp, hp, wp) through the raster or merge-window order, so the order costs only index
 // arithmetic and the stores stay row-contiguous.
+#include <type_traits>
+#include <utility>
+
 #include "pe_internal.h"
 
 namespace pe {
@@ -55,32 +62,52 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float v) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Weight pre-pack: W[E][C][Tp][P][P] -> packed[s][E/16][g][n][16 bytes] in the fragment order.
-// One thread writes one 16-byte fragment (step s, column e = 16*cb + n, lane group g).
+// Weight pre-pack: W[E][C][Tp][P][P] -> packed[s][E'/NB][g][NB][16 bytes] in the fragment order
+// (NB = 32 for bf16, 16 for fp32; columns e >= E are zero). One thread writes one 16-byte
+// fragment (k-step s, column e = NB*cb + n, lane group g).
 // ----------------------------------------------------------------------------------------
 template <typename TW>
 __global__ void pe_pack_kernel(const TW *__restrict__ w, TW *__restrict__ wpk, int P, int E,
                                int S) {
     constexpr int esz = sizeof(TW);
     constexpr int epf = 16 / esz;
+    constexpr int NB = pack_block(esz);
+    const int Ep = packed_cols(E, esz);
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)S * E * 4;
+    const int64_t total = (int64_t)S * Ep * 4;
     if (idx >= total) return;
-    const int n = (int)(idx % 16);
-    int64_t t = idx / 16;
+    const int n = (int)(idx % NB);
+    int64_t t = idx / NB;
     const int g = (int)(t % 4);
     t /= 4;
-    const int ncb = E / 16;
+    const int ncb = Ep / NB;
     const int cb = (int)(t % ncb);
     const int s = (int)(t / ncb);
-    const int e = cb * 16 + n;
+    const int e = cb * NB + n;
+    TW vals[epf];
+    if constexpr (esz == 2) {
+        // temporal-split map: g = 2j + tt, unique fragment uf = 2s + j
+        const int tt = g & 1;
+        const UFrag f = tt_frag(P, 2 * s + (g >> 1));
+#pragma unroll
+        for (int j = 0; j < epf; ++j) {
+            int u = f.u1, x = f.x1 + j;
+            bool pad = e >= E;
+            if (f.kind == kUfSplit62 && j >= 6) { u = f.u2; x = f.x2 + (j - 6); }
+            if (f.kind == kUfTail4 && j >= 4) pad = true;
+            vals[j] = pad ? TW(0) : w[((((int64_t)e * kC + u / P) * kTp + tt) * P + u % P) * P + x];
+        }
+        TW *dst = wpk + idx * epf;
+#pragma unroll
+        for (int j = 0; j < epf; ++j) dst[j] = vals[j];
+        return;
+    }
     const Piece pc = frag_piece(P, esz, s, g);
     const int first = split_first(P, esz);
-    TW vals[epf];
 #pragma unroll
     for (int j = 0; j < epf; ++j) {
         int r = 0, x = 0;
-        bool pad = false;
+        bool pad = e >= E;
         if (pc.kind == kFull) {
             r = pc.r1; x = pc.x1 + j;
         } else if (pc.kind == kSplit) {
@@ -162,18 +189,36 @@ __device__ __forceinline__ PatchRef patch_of_row(const FwdArgs &a, int row) {
     return pr;
 }
 
-template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN>
-__global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd_kernel(const FwdArgs a) {
+// Compile-time loop: f(IC<0>{}), f(IC<1>{}), ..., f(IC<N-1>{}).
+template <int N> using IC = std::integral_constant<int, N>;
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(IC<Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
+__global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs a) {
     constexpr int NT = WM * WN * 64;
     constexpr int BM = WM * TM * 16;
     constexpr int BN = WN * TN * 16;
     constexpr int S = num_steps(P, ESZ);
     constexpr int SF = full_steps(P, ESZ);
-    constexpr int STAGE = BN * 64;
-    constexpr int CH = STAGE / (16 * NT);
-    static_assert(STAGE % (16 * NT) == 0, "stage must split evenly over the threads");
+    constexpr int NSPLIT = split_frags(P, ESZ);
+    constexpr int STAGE = BN * 64;              // packed-weight bytes of one k-step
+    constexpr int CH = (STAGE / 16 + NT - 1) / NT;  // 16-byte chunks per thread per k-step
+    constexpr bool CH_EVEN = (STAGE / 16) % NT == 0;
     constexpr int FIRST = split_first(P, ESZ);  // elements in the first piece of a split fragment
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+    // epilogue staging: one 16-row block of a wave's tile, fp32; a row pitch of 4 mod 16 dwords
+    // puts the four lane groups (rows 4 apart) on disjoint banks
+    constexpr int EP_PITCH = TN * 16 + 4;       // dwords
+    constexpr int EP_WAVE = 16 * EP_PITCH * 4;  // bytes per wave
+    constexpr int KBUF = KS * STAGE;            // one LDS buffer: KS k-steps of packed weight
+    constexpr int LDS_BYTES = (2 * KBUF > EP_WAVE * WM * WN) ? 2 * KBUF : EP_WAVE * WM * WN;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
     // ---- tile: blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous run of
     // tiles so the tiles that share rows (same tm) run on one XCD, close in time.
@@ -202,49 +247,58 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd_kernel(const FwdArgs a)
         return p.base + (tt ? p.tstr : 0u) + (uint32_t)c * p.plane + (uint32_t)py * p.rstr + (uint32_t)x;
     };
 
-    // A fragments of k-step s for this lane's TM rows.
-    auto load_a = [&](int s, u32x4 (&dst)[TM]) {
+    // A fragments of k-step s for this lane's TM rows (no use of the data here: the loads stay
+    // in flight until the step's matrix products).
+    auto load_a = [&](auto sc, u32x4 (&dst)[TM]) {
+        constexpr int s = decltype(sc)::value;
         const Piece pc = frag_piece(P, ESZ, s, g);
-        if (s < SF) {
+        if constexpr (s < SF) {
 #pragma unroll
             for (int rb = 0; rb < TM; ++rb)
                 dst[rb] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(elem_off(pr[rb], pc.r1, pc.x1) * ESZ), 0, 0);
         } else {
-            const bool pad = pc.kind == kPad;
 #pragma unroll
             for (int rb = 0; rb < TM; ++rb) {
                 const int o1 = (int)(elem_off(pr[rb], pc.r1, pc.x1) * ESZ);
                 const int o2 = (int)(elem_off(pr[rb], pc.r2, pc.x2) * ESZ);
-                u32x4 v;
                 if constexpr (FIRST * ESZ == 12) {
                     const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, o1, 0, 0);
                     const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, o2, 0, 0);
-                    v = u32x4{m3.x, m3.y, m3.z, e1};
-                } else if constexpr (FIRST * ESZ == 8) {
+                    dst[rb] = u32x4{m3.x, m3.y, m3.z, e1};
+                } else {
+                    static_assert(FIRST * ESZ == 8, "split fragments are 12+4 or 8+8 bytes");
                     const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, o1, 0, 0);
                     const u32x2 e2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, o2, 0, 0);
-                    v = u32x4{m2.x, m2.y, e2.x, e2.y};
-                } else {
-                    v = u32x4{0u, 0u, 0u, 0u};
+                    dst[rb] = u32x4{m2.x, m2.y, e2.x, e2.y};
                 }
-                dst[rb] = pad ? u32x4{0u, 0u, 0u, 0u} : v;
             }
         }
     };
 
-    // Packed weight of k-step s for the tile's columns: BN*64 contiguous bytes.
+    // Packed weight of k-step s for the tile's columns: BN*64 contiguous bytes. Chunks past the
+    // last column block (or past the stage) get an offset beyond the buffer range and read 0, so
+    // the loads need no branches (branches would make the wait counts conservative).
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(a.wpk), (short)0, (int)((uint32_t)S * (uint32_t)packed_cols(a.E, ESZ) * 64u), kBufWord3);
+    uint32_t boff[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = c * NT + tid;
+        const bool ok = (CH_EVEN || idx < STAGE / 16) && (col0 >> 4) + (idx >> 6) < ncb;
+        boff[c] = ok ? ((uint32_t)(col0 >> 4) * 1024u + (uint32_t)idx * 16u) : 0x80000000u;
+    }
     auto load_b = [&](int s, u32x4 (&dst)[CH]) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.wpk) + ((int64_t)s * ncb + (col0 >> 4)) * 64;
+        const uint32_t soff = (uint32_t)s * (uint32_t)ncb * 1024u;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int idx = c * NT + tid;
-            dst[c] = ((col0 >> 4) + (idx >> 6) < ncb) ? src[idx] : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int c = 0; c < CH; ++c)
+            dst[c] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)(boff[c] + soff), 0, 0);
     };
-    auto store_b = [&](int buf, const u32x4 (&src)[CH]) {
-        u32x4 *dst = reinterpret_cast<u32x4 *>(lds + buf * STAGE);
+    // LDS position of k-step s: buffer (s / KS) & 1, slot s % KS
+    auto store_b = [&](int s, const u32x4 (&src)[CH]) {
+        u32x4 *dst = reinterpret_cast<u32x4 *>(lds + ((s / KS) & 1) * KBUF + (s % KS) * STAGE);
 #pragma unroll
-        for (int c = 0; c < CH; ++c) dst[c * NT + tid] = src[c];
+        for (int c = 0; c < CH; ++c)
+            if (CH_EVEN || c * NT + tid < STAGE / 16) dst[c * NT + tid] = src[c];
     };
 
     f32x4 acc[TM][TN];
@@ -253,11 +307,28 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd_kernel(const FwdArgs a)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf, const u32x4 (&af)[TM]) {
-        const u32x4 *bs = reinterpret_cast<const u32x4 *>(lds + buf * STAGE) + wn * TN * 64 + lane;
+    auto compute = [&](auto sc, const u32x4 (&af_in)[TM]) {
+        constexpr int s = decltype(sc)::value;
+        u32x4 af[TM];
+#pragma unroll
+        for (int rb = 0; rb < TM; ++rb) af[rb] = af_in[rb];
+        if constexpr (s >= SF && 4 * (s - SF) + 4 > NSPLIT) {
+            // the last split step holds zero (padding) fragments in its top lane groups
+            const bool pad = 4 * (s - SF) + g >= NSPLIT;
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb)
+                if (pad) af[rb] = u32x4{0u, 0u, 0u, 0u};
+        }
+        const u32x4 *bs = reinterpret_cast<const u32x4 *>(lds + ((s / KS) & 1) * KBUF + (s % KS) * STAGE) +
+                          wn * TN * 64 + lane;
+        // weight fragments are read PF column blocks ahead of their matrix products
+        u32x4 bq[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) bq[i] = bs[(i < TN ? i : 0) * 64];
 #pragma unroll
         for (int cb = 0; cb < TN; ++cb) {
-            const u32x4 bf = bs[cb * 64];
+            const u32x4 bf = bq[cb % PF];
+            if (cb + PF < TN) bq[cb % PF] = bs[(cb + PF) * 64];
 #pragma unroll
             for (int rb = 0; rb < TM; ++rb) {
                 if constexpr (ESZ == 2) {
@@ -277,40 +348,304 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd_kernel(const FwdArgs a)
         }
     };
 
-    u32x4 A0[TM], A1[TM], breg[CH];
-    load_b(0, breg);
-    load_a(0, A0);
-    if (S > 1) load_a(1, A1);
-    store_b(0, breg);
-    __syncthreads();
-    for (int s = 0; s < S; s += 2) {
-        if (s + 1 < S) load_b(s + 1, breg);
-        compute(0, A0);
-        if (s + 2 < S) load_a(s + 2, A0);
-        if (s + 1 < S) store_b(1, breg);
-        __syncthreads();
-        if (s + 1 < S) {
-            if (s + 2 < S) load_b(s + 2, breg);
-            compute(1, A1);
-            if (s + 3 < S) load_a(s + 3, A1);
-            if (s + 2 < S) store_b(0, breg);
-            __syncthreads();
+    // ---- k loop, fully unrolled. A runs AD k-steps ahead in an (AD+1)-deep register ring. The packed
+    // weight sits in two LDS buffers of KS k-steps each (one barrier per KS k-steps); while the
+    // waves compute from one buffer they fill the other, one k-step at a time, from a 2-deep
+    // register ring loaded one k-step before it is stored.
+    u32x4 Ar[AD + 1][TM], Br[2][CH];
+    {
+        u32x4 tmp[CH];
+#pragma unroll
+        for (int j = 0; j < (KS < S ? KS : S); ++j) {
+            load_b(j, tmp);
+            store_b(j, tmp);
         }
     }
+    if constexpr (KS < S) load_b(KS, Br[KS & 1]);
+    static_for<(AD < S ? AD : S)>([&](auto jc) { load_a(jc, Ar[decltype(jc)::value]); });
+    __syncthreads();
+    static_for<S>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int t = s + KS;            // the weight k-step this step moves to LDS
+        if constexpr (t + 1 < S) load_b(t + 1, Br[(t + 1) & 1]);
+        if constexpr (s + AD < S) load_a(IC<s + AD>{}, Ar[(s + AD) % (AD + 1)]);
+        compute(sc, Ar[s % (AD + 1)]);
+        if constexpr (t < S) store_b(t, Br[t & 1]);
+        if constexpr (s % KS == KS - 1 && s + 1 < S) __syncthreads();
+        // keep each step's instructions inside the step: bounds register live ranges
+        __builtin_amdgcn_sched_barrier(0);
+    });
 
-    // ---- epilogue: + bias (fp32), one RNE cast, row-contiguous output
+    // ---- epilogue: + bias (fp32), one RNE cast, 16-byte row-contiguous stores. Each wave
+    // stages one 16-row block of its tile at a time through its own LDS region.
+    __syncthreads();  // every wave is done reading the weight stages
+    float *ep = reinterpret_cast<float *>(lds + wave * EP_WAVE);
+    float bv[TN];
 #pragma unroll
     for (int cb = 0; cb < TN; ++cb) {
         const int col = col0 + (wn * TN + cb) * 16 + l16;
-        if (col >= a.E) continue;
-        const float bv = a.bias ? a.bias[col] : 0.f;
+        bv[cb] = (a.bias && col < a.E) ? a.bias[col] : 0.f;
+    }
+    constexpr int VPC = 16 / OSZ;                 // output values per 16-byte chunk
+    constexpr int CHUNKS = 16 * TN * 16 / VPC;    // chunks in a 16-row block
+    const int wcol0 = col0 + wn * TN * 16;
 #pragma unroll
-        for (int rb = 0; rb < TM; ++rb) {
+    for (int rb = 0; rb < TM; ++rb) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = row0 + (wm * TM + rb) * 16 + 4 * g + i;
-                if (row < a.n_rows) store_out<OSZ>(a.out, (int64_t)row * a.E + col, acc[rb][cb][i] + bv);
+        for (int cb = 0; cb < TN; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ep[(4 * g + i) * EP_PITCH + cb * 16 + l16] = acc[rb][cb][i] + bv[cb];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int rbase = row0 + (wm * TM + rb) * 16;
+#pragma unroll
+        for (int j = 0; j < (CHUNKS + 63) / 64; ++j) {
+            const int c = j * 64 + lane;
+            if (CHUNKS % 64 != 0 && c >= CHUNKS) break;
+            const int r = c / (TN * 16 / VPC), q = c % (TN * 16 / VPC);
+            const float *src = ep + r * EP_PITCH + q * VPC;
+            const int row = rbase + r, col = wcol0 + q * VPC;
+            if (row < a.n_rows && col < a.E) {
+                char *dst = static_cast<char *>(a.out) + ((int64_t)row * a.E + col) * OSZ;
+                if constexpr (OSZ == 2) {
+                    const f32x4 v0 = *reinterpret_cast<const f32x4 *>(src);
+                    const f32x4 v1 = *reinterpret_cast<const f32x4 *>(src + 4);
+                    u32x4 o;
+                    o.x = (uint32_t)f32_to_bf16_rne(v0.x) | ((uint32_t)f32_to_bf16_rne(v0.y) << 16);
+                    o.y = (uint32_t)f32_to_bf16_rne(v0.z) | ((uint32_t)f32_to_bf16_rne(v0.w) << 16);
+                    o.z = (uint32_t)f32_to_bf16_rne(v1.x) | ((uint32_t)f32_to_bf16_rne(v1.y) << 16);
+                    o.w = (uint32_t)f32_to_bf16_rne(v1.z) | ((uint32_t)f32_to_bf16_rne(v1.w) << 16);
+                    *reinterpret_cast<u32x4 *>(dst) = o;
+                } else {
+                    *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(src);
+                }
             }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// ----------------------------------------------------------------------------------------
+// bf16 forward kernel: 32x32x16 matrix-core blocks (see the file header)
+// ----------------------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
+__global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs a) {
+    constexpr int ESZ = 2;
+    constexpr int NT = WM * WN * 64;
+    constexpr int BM = WM * TM * 32;
+    constexpr int BN = WN * TN * 32;
+    constexpr int S = tt_steps(P);
+    constexpr int STAGE = BN * 64;                  // packed-weight bytes of one k-step
+    constexpr int CH = (STAGE / 16 + NT - 1) / NT;  // 16-byte chunks per thread per k-step
+    constexpr bool CH_EVEN = (STAGE / 16) % NT == 0;
+    // epilogue staging: 16 rows of a wave's tile at a time, fp32; a pitch of 8 mod 16 dwords
+    // puts the two lane halves (rows 4 apart) on disjoint banks
+    constexpr int EP_PITCH = TN * 32 + 8;           // dwords
+    constexpr int EP_WAVE = 16 * EP_PITCH * 4;      // bytes per wave
+    constexpr int KBUF = KS * STAGE;
+    constexpr int LDS_BYTES = (2 * KBUF > EP_WAVE * WM * WN) ? 2 * KBUF : EP_WAVE * WM * WN;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+
+    // ---- tile: blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous run of
+    // tiles so the tiles that share rows (same tm) run on one XCD, close in time.
+    const int G = a.tiles_m * a.tiles_n;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int per = G >> 3, rem = G & 7;
+    const int L = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+    const int tm = L / a.tiles_n, tn = L - tm * a.tiles_n;
+    const int row0 = tm * BM, col0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int ncb = packed_cols(a.E, ESZ) >> 5;  // 32-column blocks of the packed weight
+
+    // Per lane and 32-row block: byte offset of its patch's temporal slot h (the two lane halves
+    // read the two frames of the temporal patch: tstr = 0 for a repeated image frame). The
+    // per-step part of each address is the same for every row of the launch (one frame
+    // geometry per launch), so it is a scalar offset and the loads cost no vector arithmetic.
+    uint32_t vb[TM];
+#pragma unroll
+    for (int rb = 0; rb < TM; ++rb) {
+        const PatchRef p = patch_of_row<P>(a, row0 + (wm * TM + rb) * 32 + l32);
+        vb[rb] = (p.base + (h ? p.tstr : 0u)) * 2u;
+    }
+
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.in), (short)0, (int)a.in_bytes, kBufWord3);
+    const uint32_t plane = a.plane, rstr = a.rstr;
+
+    // A fragments of k-step s (sub-steps j = 0, 1). Loads only; the data is first used by the
+    // step's matrix products.
+    auto load_a = [&](auto sc, u32x4 (&dst)[TM][2]) {
+        constexpr int s = decltype(sc)::value;
+        static_for<2>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr UFrag f = tt_frag(P, 2 * s + j);
+            const int so1 = (int)(((uint32_t)(f.u1 / P) * plane + (uint32_t)(f.u1 % P) * rstr + f.x1) * 2u);
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb) {
+                if constexpr (f.kind == kUfFull) {
+                    dst[rb][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vb[rb], so1, 0);
+                } else if constexpr (f.kind == kUfSplit62) {
+                    const int so2 = (int)(((uint32_t)(f.u2 / P) * plane + (uint32_t)(f.u2 % P) * rstr + f.x2) * 2u);
+                    const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, (int)vb[rb], so1, 0);
+                    const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)vb[rb], so2, 0);
+                    dst[rb][j] = u32x4{m3.x, m3.y, m3.z, e1};
+                } else {
+                    const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)vb[rb], so1, 0);
+                    dst[rb][j] = u32x4{m2.x, m2.y, 0u, 0u};
+                }
+            }
+        });
+    };
+
+    // Packed weight of k-step s for the tile's columns: BN*64 contiguous bytes. Chunks past the
+    // last column block get an offset beyond the buffer range and read 0 (no branches: branches
+    // would make the wait counts conservative).
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(a.wpk), (short)0, (int)((uint32_t)S * (uint32_t)ncb * 2048u), kBufWord3);
+    uint32_t boff[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int idx = c * NT + tid;
+        const bool ok = (CH_EVEN || idx < STAGE / 16) && (col0 >> 5) + (idx >> 7) < ncb;
+        boff[c] = ok ? ((uint32_t)(col0 >> 5) * 2048u + (uint32_t)idx * 16u) : 0x80000000u;
+    }
+    auto load_b = [&](int s, u32x4 (&dst)[CH]) {
+        const uint32_t soff = (uint32_t)s * (uint32_t)ncb * 2048u;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            dst[c] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)(boff[c] + soff), 0, 0);
+    };
+    auto store_b = [&](int s, const u32x4 (&src)[CH]) {
+        u32x4 *dst = reinterpret_cast<u32x4 *>(lds + ((s / KS) & 1) * KBUF + (s % KS) * STAGE);
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            if (CH_EVEN || c * NT + tid < STAGE / 16) dst[c * NT + tid] = src[c];
+    };
+
+    // accumulators start at the bias (fp32): out = bias + sum of products
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int cb = 0; cb < TN; ++cb) {
+        const int col = col0 + (wn * TN + cb) * 32 + l32;
+        const float bv = (a.bias && col < a.E) ? a.bias[col] : 0.f;
+        f32x16 b16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b16[i] = bv;
+#pragma unroll
+        for (int rb = 0; rb < TM; ++rb) acc[rb][cb] = b16;
+    }
+
+    auto compute = [&](auto sc, const u32x4 (&af)[TM][2]) {
+        constexpr int s = decltype(sc)::value;
+        // fragment (j, cb) of this step: 1 KB at stage + (wn*TN + cb)*2 KB + j*1 KB
+        const u32x4 *bs = reinterpret_cast<const u32x4 *>(lds + ((s / KS) & 1) * KBUF + (s % KS) * STAGE) +
+                          wn * TN * 128 + lane;
+        constexpr int NF = 2 * TN;
+        u32x4 bq[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const int f = i < NF ? i : 0;
+            bq[i] = bs[(f % TN) * 128 + (f / TN) * 64];
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int j = f / TN, cb = f % TN;
+            const u32x4 bf = bq[f % PF];
+            if (f + PF < NF) bq[f % PF] = bs[((f + PF) % TN) * 128 + ((f + PF) / TN) * 64];
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb)
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, af[rb][j]), __builtin_bit_cast(bf16x8, bf), acc[rb][cb], 0, 0, 0);
+        }
+        // Pin the interleave: PF fragment reads first, then per fragment its TM products and the
+        // read PF fragments ahead (left alone, the scheduler sinks each read next to its use).
+        __builtin_amdgcn_sched_group_barrier(0x100, PF < NF ? PF : NF, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, TM, 0);
+            if (f + PF < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+
+    // ---- k loop, fully unrolled (see pe_fwd16_kernel for the pipeline).
+    u32x4 Ar[AD + 1][TM][2], Br[2][CH];
+    {
+        u32x4 tmp[CH];
+#pragma unroll
+        for (int j = 0; j < (KS < S ? KS : S); ++j) {
+            load_b(j, tmp);
+            store_b(j, tmp);
+        }
+    }
+    if constexpr (KS < S) load_b(KS, Br[KS & 1]);
+    static_for<(AD < S ? AD : S)>([&](auto jc) { load_a(jc, Ar[decltype(jc)::value]); });
+    __syncthreads();
+    static_for<S>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int t = s + KS;
+        if constexpr (t + 1 < S) load_b(t + 1, Br[(t + 1) & 1]);
+        if constexpr (s + AD < S) load_a(IC<s + AD>{}, Ar[(s + AD) % (AD + 1)]);
+        compute(sc, Ar[s % (AD + 1)]);
+        if constexpr (t < S) store_b(t, Br[t & 1]);
+        if constexpr (s % KS == KS - 1 && s + 1 < S) __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // ---- epilogue: one RNE cast, 16-byte row-contiguous stores. Lane l holds column l % 32
+    // and, in accumulator element i, row 8*(i/4) + 4*(l/32) + i%4 of its block.
+    __syncthreads();
+    float *ep = reinterpret_cast<float *>(lds + wave * EP_WAVE);
+    constexpr int VPC = 16 / OSZ;                 // output values per 16-byte chunk
+    constexpr int RCH = TN * 32 / VPC;            // chunks per row
+    constexpr int CHUNKS = 16 * RCH;              // chunks in 16 rows
+    const int wcol0 = col0 + wn * TN * 32;
+#pragma unroll
+    for (int rb = 0; rb < TM; ++rb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int cb = 0; cb < TN; ++cb)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int i = half * 8 + q;
+                    const int rl = 8 * (q / 4) + 4 * h + (q % 4);   // row within these 16
+                    ep[rl * EP_PITCH + cb * 32 + l32] = acc[rb][cb][i];
+                }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are in LDS
+            __builtin_amdgcn_wave_barrier();
+            const int rbase = row0 + (wm * TM + rb) * 32 + half * 16;
+#pragma unroll
+            for (int jj = 0; jj < (CHUNKS + 63) / 64; ++jj) {
+                const int c = jj * 64 + lane;
+                if (CHUNKS % 64 != 0 && c >= CHUNKS) break;
+                const int r = c / RCH, qq = c % RCH;
+                const float *src = ep + r * EP_PITCH + qq * VPC;
+                const int row = rbase + r, col = wcol0 + qq * VPC;
+                if (row < a.n_rows && col < a.E) {
+                    char *dst = static_cast<char *>(a.out) + ((int64_t)row * a.E + col) * OSZ;
+                    if constexpr (OSZ == 2) {
+                        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(src);
+                        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(src + 4);
+                        u32x4 o;
+                        o.x = (uint32_t)f32_to_bf16_rne(v0.x) | ((uint32_t)f32_to_bf16_rne(v0.y) << 16);
+                        o.y = (uint32_t)f32_to_bf16_rne(v0.z) | ((uint32_t)f32_to_bf16_rne(v0.w) << 16);
+                        o.z = (uint32_t)f32_to_bf16_rne(v1.x) | ((uint32_t)f32_to_bf16_rne(v1.y) << 16);
+                        o.w = (uint32_t)f32_to_bf16_rne(v1.z) | ((uint32_t)f32_to_bf16_rne(v1.w) << 16);
+                        *reinterpret_cast<u32x4 *>(dst) = o;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(src);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -319,8 +654,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd_kernel(const FwdArgs a)
 // Launchers
 // ----------------------------------------------------------------------------------------
 hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, hipStream_t st) {
-    const int S = num_steps(P, w_esz);
-    const int64_t total = (int64_t)S * E * 4;
+    const int S = packed_steps(P, w_esz);
+    const int64_t total = (int64_t)S * packed_cols(E, w_esz) * 4;
     const int threads = 256;
     const int blocks = (int)((total + threads - 1) / threads);
     if (w_esz == 2)
@@ -343,24 +678,37 @@ hipError_t launch_bias(const void *b, int b_esz, float *bias32, int E, hipStream
     return hipGetLastError();
 }
 
-template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN>
-static hipError_t launch_cfg(FwdArgs a, hipStream_t st) {
+template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
+static hipError_t launch16(FwdArgs a, hipStream_t st) {
     constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
-    const int blocks = a.tiles_m * a.tiles_n;
-    hipLaunchKernelGGL((pe_fwd_kernel<P, ESZ, OSZ, TM, TN, WM, WN>), dim3(blocks), dim3(WM * WN * 64), 0, st, a);
+    hipLaunchKernelGGL((pe_fwd16_kernel<P, ESZ, OSZ, TM, TN, WM, WN, KS, PF, AD>), dim3(a.tiles_m * a.tiles_n),
+                       dim3(WM * WN * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
+static hipError_t launch32(FwdArgs a, hipStream_t st) {
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    a.tiles_m = (a.n_rows + BM - 1) / BM;
+    a.tiles_n = (a.E + BN - 1) / BN;
+    hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD>), dim3(a.tiles_m * a.tiles_n),
+                       dim3(WM * WN * 64), 0, st, a);
     return hipGetLastError();
 }
 
 // Tile choice: the largest tile that still gives every CU work.
 template <int P, int ESZ, int OSZ>
 static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
-    const int64_t big = ((int64_t)(a.n_rows + 255) / 256) * ((a.E + 255) / 256);
-    const int64_t mid = ((int64_t)(a.n_rows + 63) / 64) * ((a.E + 255) / 256);
-    if (big >= 512) return launch_cfg<P, ESZ, OSZ, 4, 8, 4, 2>(a, st);
-    if (mid >= 256) return launch_cfg<P, ESZ, OSZ, 2, 8, 2, 2>(a, st);
-    return launch_cfg<P, ESZ, OSZ, 1, 4, 2, 2>(a, st);
+    if constexpr (ESZ == 4) {
+        // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps)
+        return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
+    } else {
+        const int64_t big = ((int64_t)(a.n_rows + 255) / 256) * ((a.E + 255) / 256);
+        if (big >= 512) return launch32<P, OSZ, 2, 8, 4, 1, 2, 4, 2>(a, st);
+        return launch32<P, OSZ, 1, 2, 2, 2, 2, 2, 2>(a, st);
+    }
 }
 
 hipError_t launch_forward(const FwdArgs &a, int P, int in_esz, int out_esz, hipStream_t st) {
