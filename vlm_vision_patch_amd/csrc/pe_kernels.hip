@@ -431,7 +431,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs 
 // ----------------------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
+template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD>
 __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs a) {
     constexpr int ESZ = 2;
     constexpr int NT = WM * WN * 64;
@@ -574,8 +574,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         }
     };
 
-    // ---- k loop, fully unrolled (see pe_fwd16_kernel for the pipeline).
-    u32x4 Ar[AD + 1][TM][2], Br[2][CH];
+    // ---- k loop, fully unrolled. A runs AD k-steps ahead in an (AD+1)-deep register ring. The
+    // packed weight sits in two LDS buffers of KS k-steps each (one barrier per KS k-steps);
+    // while the waves compute from one buffer they fill the other one k-step at a time from a
+    // BD-deep register ring (each weight k-step is loaded BD-1 k-steps before it is stored).
+    u32x4 Ar[AD + 1][TM][2], Br[BD][CH];
     {
         u32x4 tmp[CH];
 #pragma unroll
@@ -584,16 +587,19 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
             store_b(j, tmp);
         }
     }
-    if constexpr (KS < S) load_b(KS, Br[KS & 1]);
+    static_for<BD - 1>([&](auto ic) {
+        constexpr int t = KS + decltype(ic)::value;
+        if constexpr (t < S) load_b(t, Br[t % BD]);
+    });
     static_for<(AD < S ? AD : S)>([&](auto jc) { load_a(jc, Ar[decltype(jc)::value]); });
     __syncthreads();
     static_for<S>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         constexpr int t = s + KS;
-        if constexpr (t + 1 < S) load_b(t + 1, Br[(t + 1) & 1]);
+        if constexpr (t + BD - 1 < S) load_b(t + BD - 1, Br[(t + BD - 1) % BD]);
         if constexpr (s + AD < S) load_a(IC<s + AD>{}, Ar[(s + AD) % (AD + 1)]);
         compute(sc, Ar[s % (AD + 1)]);
-        if constexpr (t < S) store_b(t, Br[t & 1]);
+        if constexpr (t < S) store_b(t, Br[t % BD]);
         if constexpr (s % KS == KS - 1 && s + 1 < S) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -688,12 +694,12 @@ static hipError_t launch16(FwdArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
+template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD>
 static hipError_t launch32(FwdArgs a, hipStream_t st) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
-    hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD>), dim3(a.tiles_m * a.tiles_n),
+    hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD, BD>), dim3(a.tiles_m * a.tiles_n),
                        dim3(WM * WN * 64), 0, st, a);
     return hipGetLastError();
 }
@@ -706,8 +712,8 @@ static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
         return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
     } else {
         const int64_t big = ((int64_t)(a.n_rows + 255) / 256) * ((a.E + 255) / 256);
-        if (big >= 512) return launch32<P, OSZ, 2, 8, 4, 1, 2, 4, 2>(a, st);
-        return launch32<P, OSZ, 1, 2, 2, 2, 2, 2, 2>(a, st);
+        if (big >= 512) return launch32<P, OSZ, 2, 8, 4, 1, 2, 4, 2, 3>(a, st);
+        return launch32<P, OSZ, 1, 2, 2, 2, 2, 2, 2, 3>(a, st);
     }
 }
 
