@@ -153,6 +153,10 @@ def main():
     ap.add_argument("--extra", type=str, default="5",
                     help="comma-separated further workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time K launches from Python instead of a captured graph (for counter runs)")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus,
@@ -164,7 +168,17 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
 
-    r = time_workload(args.workload, args.steps, args.warmup)
+    if args.copy_calibrate:
+        n = args.copy_calibrate // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4}), flush=True)
+        return
+
+    r = time_workload(args.workload, args.steps, args.warmup, graph=not args.eager)
     wl = r["wl"]
     t_s = r["ms"] / 1e3
     tflops = r["flops"] / t_s / 1e12
@@ -174,14 +188,15 @@ def main():
     ai = r["flops"] / r["bytes"]
     ridge = peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9)
     bound = "mfma" if ai >= ridge else "hbm"
-    traffic = load_traffic("pe_fwd_kernel", wl.name)
+    kname = "pe_fwd32_kernel" if bf16 else "pe_fwd16_kernel"
+    traffic = load_traffic(kname, wl.name)
     roof = {"bound": bound,
             "achieved": round(tflops if bound == "mfma" else gbs, 3),
             "peak": peak_fl if bound == "mfma" else PEAK_HBM_GBS,
             "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
             "frac": round((tflops / peak_fl) if bound == "mfma" else (gbs / PEAK_HBM_GBS), 4),
             "traffic": traffic,
-            "kernel": "pe_fwd_kernel",
+            "kernel": kname,
             "per_launch": {"flops": r["flops"], "alg_bytes": r["bytes"], "avg_us": round(r["ms"] * 1e3, 3)},
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     also = {}
@@ -189,7 +204,7 @@ def main():
         if e == args.workload:
             continue
         st = max(5, min(args.steps, 50))
-        q = time_workload(e, st, 3)
+        q = time_workload(e, st, 3, graph=not args.eager)
         qt = q["ms"] / 1e3
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
         also[q["wl"].name] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),

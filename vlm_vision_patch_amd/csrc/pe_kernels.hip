@@ -711,9 +711,12 @@ static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
         // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps)
         return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
     } else {
+        // 256 x 256 tiles (4 waves of 64 x 256) once there are enough of them to occupy about half
+        // the CUs; below that, 64 x 128 tiles (4 waves of 32 x 64). Measured on workloads of
+        // 1k, 8k and 332k patches.
         const int64_t big = ((int64_t)(a.n_rows + 255) / 256) * ((a.E + 255) / 256);
-        if (big >= 512) return launch32<P, OSZ, 2, 8, 4, 1, 2, 4, 2, 3>(a, st);
-        return launch32<P, OSZ, 1, 2, 2, 2, 2, 2, 2, 3>(a, st);
+        if (big >= 128) return launch32<P, OSZ, 2, 8, 4, 1, 2, 4, 2, 3>(a, st);
+        return launch32<P, OSZ, 1, 2, 2, 2, 4, 2, 2, 3>(a, st);
     }
 }
 
