@@ -232,6 +232,7 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
             a.out = static_cast<char *>(out) + r * E * oes;
             a.n_rows = (int32_t)nr;
             a.n_items = 0;
+            a.colmajor = (uint64_t)nr * K * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
             hipError_t e = pe::launch_forward(a, P, ies, oes, st);
             if (e != hipSuccess) return hip_fail(e, "forward launch");
         }
@@ -259,6 +260,7 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         a.out = static_cast<char *>(out) + row0[i0] * E * oes;
         a.n_rows = (int32_t)(row0[i1] - row0[i0]);
         a.n_items = i1 - i0;
+        a.colmajor = (uint64_t)span * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
         int64_t off = 0;
         for (int i = i0; i < i1; ++i) {
             pe::Item &it = a.items[i - i0];

@@ -33,6 +33,7 @@ struct FwdArgs {
     int32_t m;           // merge size
     int32_t n_items;
     int32_t tiles_m, tiles_n;
+    int32_t colmajor;      // tile order within an XCD's run: 1 = column tiles outermost
     uint32_t plane, rstr;  // channel and pixel-row strides (elements), the same for every row
     Item items[kMaxItems];
 };

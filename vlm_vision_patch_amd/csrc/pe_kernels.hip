@@ -227,7 +227,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs 
     const int xcd = bid & 7, loc = bid >> 3;
     const int per = G >> 3, rem = G & 7;
     const int L = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
-    const int tm = L / a.tiles_n, tn = L - tm * a.tiles_n;
+    // row-major runs share rows (A) within an XCD; column-major runs share weight columns, for
+    // launches whose input is smaller than the weight
+    const int tm = a.colmajor ? L % a.tiles_m : L / a.tiles_n;
+    const int tn = a.colmajor ? L / a.tiles_m : L % a.tiles_n;
     const int row0 = tm * BM, col0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -456,7 +459,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     const int xcd = bid & 7, loc = bid >> 3;
     const int per = G >> 3, rem = G & 7;
     const int L = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
-    const int tm = L / a.tiles_n, tn = L - tm * a.tiles_n;
+    // row-major runs share rows (A) within an XCD; column-major runs share weight columns, for
+    // launches whose input is smaller than the weight
+    const int tm = a.colmajor ? L % a.tiles_m : L / a.tiles_n;
+    const int tn = a.colmajor ? L / a.tiles_m : L % a.tiles_n;
     const int row0 = tm * BM, col0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -657,6 +663,175 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 }
 
 // ----------------------------------------------------------------------------------------
+// bf16 split-K kernel for few rows: the four waves of a workgroup share one BM x BN tile and
+// each takes a contiguous quarter of the k-steps, so each wave's chain of dependent k-steps is a
+// quarter as long. A wave's weight fragments are its own (no other wave uses that k range): they
+// go from global memory straight to registers, with no LDS stage and no barrier in the k loop.
+// The four fp32 partial tiles meet in LDS at the end and are summed in a fixed order.
+// ----------------------------------------------------------------------------------------
+template <int P, int OSZ, int TM, int TN, int AD>
+__global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
+    constexpr int NW = 4;
+    constexpr int BM = TM * 32, BN = TN * 32;
+    constexpr int S = tt_steps(P);
+    constexpr int PITCH = BN + 8;                   // dwords per partial-tile row (8 mod 16)
+    constexpr int PART = BM * PITCH * 4;            // bytes per wave's partial tile
+    __shared__ __attribute__((aligned(16))) unsigned char lds[NW * PART];
+
+    const int G = a.tiles_m * a.tiles_n;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int per = G >> 3, rem = G & 7;
+    const int L = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+    // row-major runs share rows (A) within an XCD; column-major runs share weight columns, for
+    // launches whose input is smaller than the weight
+    const int tm = a.colmajor ? L % a.tiles_m : L / a.tiles_n;
+    const int tn = a.colmajor ? L / a.tiles_m : L % a.tiles_n;
+    const int row0 = tm * BM, col0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int ncb = packed_cols(a.E, 2) >> 5;
+
+    uint32_t vb[TM];
+#pragma unroll
+    for (int rb = 0; rb < TM; ++rb) {
+        const PatchRef p = patch_of_row<P>(a, row0 + rb * 32 + l32);
+        vb[rb] = (p.base + (h ? p.tstr : 0u)) * 2u;
+    }
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.in), (short)0, (int)a.in_bytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(a.wpk), (short)0, (int)((uint32_t)S * (uint32_t)ncb * 2048u), kBufWord3);
+    const uint32_t plane = a.plane, rstr = a.rstr;
+    // weight fragment (s, j, cb): 1 KB at ((s*ncb + cb)*2 + j) KB; column blocks past E read 0
+    uint32_t wb[TN];
+#pragma unroll
+    for (int cb = 0; cb < TN; ++cb)
+        wb[cb] = ((col0 >> 5) + cb < ncb) ? ((uint32_t)((col0 >> 5) + cb) * 2048u + (uint32_t)lane * 16u) : 0x80000000u;
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int cb = 0; cb < TN; ++cb) {
+        const int col = col0 + cb * 32 + l32;
+        const float bv = (wave == 0 && a.bias && col < a.E) ? a.bias[col] : 0.f;
+        f32x16 b16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b16[i] = bv;
+#pragma unroll
+        for (int rb = 0; rb < TM; ++rb) acc[rb][cb] = b16;
+    }
+
+    struct Frags { u32x4 a[TM][2]; u32x4 b[TN][2]; };
+    auto load = [&](auto sc, Frags &d) {
+        constexpr int s = decltype(sc)::value;
+        static_for<2>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr UFrag f = tt_frag(P, 2 * s + j);
+            const int so1 = (int)(((uint32_t)(f.u1 / P) * plane + (uint32_t)(f.u1 % P) * rstr + f.x1) * 2u);
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb) {
+                if constexpr (f.kind == kUfFull) {
+                    d.a[rb][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vb[rb], so1, 0);
+                } else if constexpr (f.kind == kUfSplit62) {
+                    const int so2 = (int)(((uint32_t)(f.u2 / P) * plane + (uint32_t)(f.u2 % P) * rstr + f.x2) * 2u);
+                    const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, (int)vb[rb], so1, 0);
+                    const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)vb[rb], so2, 0);
+                    d.a[rb][j] = u32x4{m3.x, m3.y, m3.z, e1};
+                } else {
+                    const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)vb[rb], so1, 0);
+                    d.a[rb][j] = u32x4{m2.x, m2.y, 0u, 0u};
+                }
+            }
+            const int sw = (int)(((uint32_t)s * (uint32_t)ncb * 2u + j) * 1024u);
+#pragma unroll
+            for (int cb = 0; cb < TN; ++cb) d.b[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)wb[cb], sw, 0);
+        });
+    };
+    auto mma = [&](const Frags &d) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int cb = 0; cb < TN; ++cb)
+#pragma unroll
+                for (int rb = 0; rb < TM; ++rb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, d.a[rb][j]), __builtin_bit_cast(bf16x8, d.b[cb][j]), acc[rb][cb], 0, 0, 0);
+    };
+    // wave W: k-steps [W*S/NW, (W+1)*S/NW), loads AD steps ahead in an (AD+1)-deep ring
+    auto run = [&](auto wc) {
+        constexpr int W = decltype(wc)::value;
+        constexpr int lo = W * S / NW, hi = (W + 1) * S / NW, n = hi - lo;
+        Frags ring[AD + 1];
+        static_for<(AD < n ? AD : n)>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            load(IC<lo + i>{}, ring[i]);
+        });
+        static_for<n>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i + AD < n) load(IC<lo + i + AD>{}, ring[(i + AD) % (AD + 1)]);
+            mma(ring[i % (AD + 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    switch (wave) {
+        case 0: run(IC<0>{}); break;
+        case 1: run(IC<1>{}); break;
+        case 2: run(IC<2>{}); break;
+        default: run(IC<3>{}); break;
+    }
+
+    // ---- partial tiles to LDS, then each wave sums BM/NW rows of the four partials (fixed
+    // order), one RNE cast, 16-byte row-contiguous stores
+    float *part = reinterpret_cast<float *>(lds + wave * PART);
+#pragma unroll
+    for (int rb = 0; rb < TM; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < TN; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = rb * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+                part[r * PITCH + cb * 32 + l32] = acc[rb][cb][i];
+            }
+    __syncthreads();
+    constexpr int VPC = 16 / OSZ;                   // output values per 16-byte chunk
+    constexpr int RCH = BN / VPC;                   // chunks per row
+    constexpr int ROWS = BM / NW;                   // rows per wave
+    constexpr int CHUNKS = ROWS * RCH;
+    const float *p0 = reinterpret_cast<const float *>(lds);
+#pragma unroll
+    for (int jj = 0; jj < (CHUNKS + 63) / 64; ++jj) {
+        const int c = jj * 64 + lane;
+        if (CHUNKS % 64 != 0 && c >= CHUNKS) break;
+        const int r = wave * ROWS + c / RCH, q = c % RCH;
+        const int row = row0 + r, col = col0 + q * VPC;
+        if (row < a.n_rows && col < a.E) {
+            float v[VPC];
+#pragma unroll
+            for (int e4 = 0; e4 < VPC; e4 += 4) {
+                f32x4 t = *reinterpret_cast<const f32x4 *>(p0 + r * PITCH + q * VPC + e4);
+#pragma unroll
+                for (int w = 1; w < NW; ++w)
+                    t += *reinterpret_cast<const f32x4 *>(p0 + w * (PART / 4) + r * PITCH + q * VPC + e4);
+                v[e4] = t.x; v[e4 + 1] = t.y; v[e4 + 2] = t.z; v[e4 + 3] = t.w;
+            }
+            char *dst = static_cast<char *>(a.out) + ((int64_t)row * a.E + col) * OSZ;
+            if constexpr (OSZ == 2) {
+                u32x4 o;
+                o.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+                o.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+                o.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
+                o.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+                *reinterpret_cast<u32x4 *>(dst) = o;
+            } else {
+                *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------------------
 hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, hipStream_t st) {
@@ -704,6 +879,15 @@ static hipError_t launch32(FwdArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int P, int OSZ, int TM, int TN, int AD>
+static hipError_t launch_sk(FwdArgs a, hipStream_t st) {
+    constexpr int BM = TM * 32, BN = TN * 32;
+    a.tiles_m = (a.n_rows + BM - 1) / BM;
+    a.tiles_n = (a.E + BN - 1) / BN;
+    hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, OSZ, TM, TN, AD>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 // Tile choice: the largest tile that still gives every CU work.
 template <int P, int ESZ, int OSZ>
 static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
@@ -716,7 +900,9 @@ static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
         // 1k, 8k and 332k patches.
         const int64_t big = ((int64_t)(a.n_rows + 255) / 256) * ((a.E + 255) / 256);
         if (big >= 128) return launch32<P, OSZ, 2, 8, 4, 1, 2, 4, 2, 3>(a, st);
-        return launch32<P, OSZ, 1, 2, 2, 2, 4, 2, 2, 3>(a, st);
+        // few rows: split-K workgroups, 32 rows by 160 (or 128) columns
+        if (a.E % 160 == 0) return launch_sk<P, OSZ, 1, 5, 2>(a, st);
+        return launch_sk<P, OSZ, 1, 4, 2>(a, st);
     }
 }
 
