@@ -418,9 +418,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs 
                     o.y = (uint32_t)f32_to_bf16_rne(v0.z) | ((uint32_t)f32_to_bf16_rne(v0.w) << 16);
                     o.z = (uint32_t)f32_to_bf16_rne(v1.x) | ((uint32_t)f32_to_bf16_rne(v1.y) << 16);
                     o.w = (uint32_t)f32_to_bf16_rne(v1.z) | ((uint32_t)f32_to_bf16_rne(v1.w) << 16);
-                    *reinterpret_cast<u32x4 *>(dst) = o;
+                    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
                 } else {
-                    *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(src);
+                    __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(src), reinterpret_cast<f32x4 *>(dst));
                 }
             }
         }
@@ -610,7 +610,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         __builtin_amdgcn_sched_barrier(0);
     });
 
-    // ---- epilogue: one RNE cast, 16-byte row-contiguous stores. Lane l holds column l % 32
+    // ---- epilogue: one RNE cast, 16-byte row-contiguous non-temporal stores (the output is
+    // not read again here; keeping it out of L2 leaves room for the weight). Lane l holds column l % 32
     // and, in accumulator element i, row 8*(i/4) + 4*(l/32) + i%4 of its block.
     __syncthreads();
     float *ep = reinterpret_cast<float *>(lds + wave * EP_WAVE);
@@ -650,9 +651,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
                         o.y = (uint32_t)f32_to_bf16_rne(v0.z) | ((uint32_t)f32_to_bf16_rne(v0.w) << 16);
                         o.z = (uint32_t)f32_to_bf16_rne(v1.x) | ((uint32_t)f32_to_bf16_rne(v1.y) << 16);
                         o.w = (uint32_t)f32_to_bf16_rne(v1.z) | ((uint32_t)f32_to_bf16_rne(v1.w) << 16);
-                        *reinterpret_cast<u32x4 *>(dst) = o;
+                        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
                     } else {
-                        *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(src);
+                        __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(src), reinterpret_cast<f32x4 *>(dst));
                     }
                 }
             }
@@ -823,9 +824,9 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
                 o.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
                 o.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
                 o.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
-                *reinterpret_cast<u32x4 *>(dst) = o;
+                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
             } else {
-                *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+                __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(dst));
             }
         }
     }
@@ -895,11 +896,10 @@ static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
         // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps)
         return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
     } else {
-        // 256 x 256 tiles (4 waves of 64 x 256) once there are enough of them to occupy about half
-        // the CUs; below that, 64 x 128 tiles (4 waves of 32 x 64). Measured on workloads of
-        // 1k, 8k and 332k patches.
+        // 256 x 256 tiles (8 waves of 32 x 256, two per SIMD) once there are enough of them to
+        // occupy about half the CUs. Measured on workloads of 1k, 8k and 332k patches.
         const int64_t big = ((int64_t)(a.n_rows + 255) / 256) * ((a.E + 255) / 256);
-        if (big >= 128) return launch32<P, OSZ, 2, 8, 4, 1, 2, 4, 2, 3>(a, st);
+        if (big >= 128) return launch32<P, OSZ, 1, 8, 8, 1, 2, 4, 2, 3>(a, st);
         // few rows: split-K workgroups, 32 rows by 160 (or 128) columns
         if (a.E % 160 == 0) return launch_sk<P, OSZ, 1, 5, 2>(a, st);
         return launch_sk<P, OSZ, 1, 4, 2>(a, st);
