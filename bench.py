@@ -50,6 +50,19 @@ def algorithmic(wl):
     return n, flops, byts
 
 
+def dominant_kernel(wl):
+    """Name of the kernel that does the step's work. The library picks it per launch from the
+    launch's size: bf16 launches with at least 128 tiles of 256 x 256 outputs run the large-tile
+    kernel, smaller ones the split-k kernel; fp32 runs the 16x16 kernel. A frames launch holds at
+    most 64 items; the largest launch decides."""
+    if wl.w_dtype != "bf16":
+        return "pe_fwd16_kernel"
+    rows = [t * h * w for (t, h, w) in wl.grid]
+    per_launch = max(sum(rows[i:i + 64]) for i in range(0, len(rows), 64))
+    tiles = ((per_launch + 255) // 256) * ((wl.embed + 255) // 256)
+    return "pe_fwd32_kernel" if tiles >= 128 else "pe_fwd32_sk_kernel"
+
+
 def time_workload(idx, steps, warmup, graph=True):
     import torch
     import workloads
@@ -188,7 +201,7 @@ def main():
     ai = r["flops"] / r["bytes"]
     ridge = peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9)
     bound = "mfma" if ai >= ridge else "hbm"
-    kname = "pe_fwd32_kernel" if bf16 else "pe_fwd16_kernel"
+    kname = dominant_kernel(wl)
     traffic = load_traffic(kname, wl.name)
     roof = {"bound": bound,
             "achieved": round(tflops if bound == "mfma" else gbs, 3),
