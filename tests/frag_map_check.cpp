@@ -61,8 +61,30 @@ static int check_tt(int P) {
     return pads == 2 * S * 8 - rows * P ? 0 : 1;
 }
 
+// The patch-rows map: lane group g of k-step s takes elements [32s + 8g, +8) of the stored row,
+// so each k-step covers 32 consecutive elements and only the tail past K is padding.
+static int check_rows(int P) {
+    using namespace pe;
+    const int K = kC * kTp * P * P, S = rows_steps(P);
+    std::vector<int> hits(K, 0);
+    int pads = 0;
+    for (int s = 0; s < S; ++s)
+        for (int g = 0; g < 4; ++g)
+            for (int j = 0; j < 8; ++j) {
+                const int k = 32 * s + 8 * g + j;
+                if (k >= K) ++pads; else hits[k]++;
+            }
+    for (int k = 0; k < K; ++k)
+        if (hits[k] != 1) { printf("rows map P%d element %d hit %d times\n", P, k, hits[k]); return 1; }
+    if (pads >= 32) { printf("rows map P%d: a whole padded k-step\n", P); return 1; }
+    printf("rows map P%d: %d steps, %d pad elements\n", P, S, pads);
+    return 0;
+}
+
 int main() {
     int bad = 0;
+    for (int P : {14, 16}) bad |= check_rows(P);
+    if (pe::rows_steps(14) != 37 || pe::rows_steps(16) != 48) { printf("rows step counts\n"); bad = 1; }
     for (int P : {14, 16})
         for (int esz : {2, 4}) bad |= check(P, esz);
     for (int P : {14, 16}) bad |= check_tt(P);

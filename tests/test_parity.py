@@ -160,7 +160,8 @@ def test_frames_edge_cases(pe, case):
                                        (16, 777, torch.bfloat16, torch.float32),
                                        (14, 300, torch.float32, torch.float32),
                                        (16, 65, torch.float32, torch.float32),
-                                       (14, 20000, torch.bfloat16, torch.bfloat16)])
+                                       (14, 20000, torch.bfloat16, torch.bfloat16),
+                                       (16, 9000, torch.bfloat16, torch.bfloat16)])
 def test_patch_rows(pe, P, N, dt, od):
     K = 3 * 2 * P * P
     x = make(300 + N, (N, K), dt)

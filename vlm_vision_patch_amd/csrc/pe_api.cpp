@@ -17,7 +17,8 @@ struct pe_handle_s {
     pe_config cfg;
     int device;
     int steps;
-    void *wpk;      // packed weight, steps * packed_cols(E) * 64 bytes
+    void *wpk;      // packed weight for frames, steps * packed_cols(E) * 64 bytes
+    void *wpk_rows; // bf16: the same weight packed for patch rows (inside wpk's allocation); fp32: wpk
     float *bias32;  // fp32 bias or null
 };
 
@@ -110,7 +111,10 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const int wes = esize(cfg->weight_dtype);
     const int steps = pe::packed_steps(cfg->patch_size, wes);
-    const size_t wpk_bytes = (size_t)steps * pe::packed_cols(cfg->embed_dim, wes) * 64;
+    const size_t frames_bytes = (size_t)steps * pe::packed_cols(cfg->embed_dim, wes) * 64;
+    // bf16 keeps a second pack in the patch-rows order (fp32 uses one map for both inputs)
+    const size_t rows_bytes = wes == 2 ? (size_t)pe::rows_steps(cfg->patch_size) * pe::packed_cols(cfg->embed_dim, wes) * 64 : 0;
+    const size_t wpk_bytes = frames_bytes + rows_bytes;
 
     pe_handle h = new (std::nothrow) pe_handle_s;
     if (!h) return fail(PE_ERR_OOM, "host allocation failed");
@@ -118,6 +122,7 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     h->device = dev;
     h->steps = steps;
     h->wpk = nullptr;
+    h->wpk_rows = nullptr;
     h->bias32 = nullptr;
     e = hipMalloc(&h->wpk, wpk_bytes);
     if (e != hipSuccess) {
@@ -125,6 +130,7 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
         (void)hipGetLastError();
         return fail(PE_ERR_OOM, "hipMalloc(%zu) for the packed weight: %s", wpk_bytes, hipGetErrorString(e));
     }
+    h->wpk_rows = rows_bytes ? static_cast<char *>(h->wpk) + frames_bytes : h->wpk;
     if (bias) {
         e = hipMalloc(reinterpret_cast<void **>(&h->bias32), sizeof(float) * cfg->embed_dim);
         if (e != hipSuccess) {
@@ -134,7 +140,9 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
             return fail(PE_ERR_OOM, "hipMalloc for the bias: %s", hipGetErrorString(e));
         }
     }
-    e = pe::launch_pack(weight, wes, h->wpk, cfg->patch_size, cfg->embed_dim, st);
+    e = pe::launch_pack(weight, wes, h->wpk, cfg->patch_size, cfg->embed_dim, false, st);
+    if (e == hipSuccess && rows_bytes)
+        e = pe::launch_pack(weight, wes, h->wpk_rows, cfg->patch_size, cfg->embed_dim, true, st);
     if (e == hipSuccess && bias) e = pe::launch_bias(bias, wes, h->bias32, cfg->embed_dim, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
@@ -225,6 +233,7 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         for (int64_t r = 0; r < N; r += rows_per) {
             const int64_t nr = (N - r < rows_per) ? N - r : rows_per;
             a.kind = 0;
+            a.wpk = h->wpk_rows;
             a.plane = (uint32_t)(pe::kTp * P * P);  // a row is [C][Tp][P][P]
             a.rstr = (uint32_t)P;
             a.in = static_cast<const char *>(input) + r * K * ies;
@@ -239,8 +248,9 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         return PE_OK;
     }
 
-    // frames: launches of at most kMaxItems consecutive items of one frame geometry (h, w) and
-    // at most kMaxLaunchBytes of input
+    // frames: launches of at most kMaxItems consecutive items of one frame geometry (h, w), all
+    // single images or all not (the kernels load an image's shared temporal slots once), and at
+    // most kMaxLaunchBytes of input
     int64_t x0 = 0;  // element offset of item i0
     int i0 = 0;
     while (i0 < n_items) {
@@ -248,11 +258,14 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         int64_t span = 0;
         while (i1 < n_items && i1 - i0 < pe::kMaxItems &&
                grid_thw[3 * i1 + 1] == grid_thw[3 * i0 + 1] && grid_thw[3 * i1 + 2] == grid_thw[3 * i0 + 2] &&
+               (F[i1] == 1) == (F[i0] == 1) &&
                (uint64_t)(span + elems[i1]) * ies <= kMaxLaunchBytes) {
             span += elems[i1];
             ++i1;
         }
         a.kind = 1;
+        a.wpk = h->wpk;
+        a.img = F[i0] == 1 ? 1 : 0;
         a.rstr = (uint32_t)grid_thw[3 * i0 + 2] * (uint32_t)P;
         a.plane = (uint32_t)grid_thw[3 * i0 + 1] * (uint32_t)P * a.rstr;
         a.in = static_cast<const char *>(input) + x0 * ies;

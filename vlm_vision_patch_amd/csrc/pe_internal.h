@@ -34,6 +34,7 @@ struct FwdArgs {
     int32_t n_items;
     int32_t tiles_m, tiles_n;
     int32_t colmajor;      // tile order within an XCD's run: 1 = column tiles outermost
+    int32_t img;           // 1: frames launch whose items are all single images (F = 1)
     uint32_t plane, rstr;  // channel and pixel-row strides (elements), the same for every row
     Item items[kMaxItems];
 };
@@ -152,13 +153,24 @@ __host__ __device__ constexpr UFrag tt_frag(int P, int uf) {
     return f;
 }
 
+// bf16 patch-rows map: a patch row is stored in (c, t, py, px) order, so k-step s and lane
+// group g take its elements [32s + 8g, 32s + 8g + 8): every load is 16 contiguous bytes and a
+// k-step reads 64 contiguous bytes of each row. Elements at K and beyond are zero in the packed
+// weight (P = 14: the last lane group of step 36).
+__host__ __device__ constexpr int rows_steps(int P) { return (kC * kTp * P * P + 31) / 32; }
+
 // k-steps of the packed weight: the temporal-split map for bf16, frag_piece's map for fp32
 __host__ __device__ constexpr int packed_steps(int P, int esz) {
     return esz == 2 ? tt_steps(P) : num_steps(P, esz);
 }
 
+// How the bf16 kernels read A: frames with two temporal slots, frames that are all single images
+// (both slots the same pixels), or pre-flattened patch rows (the rows map above).
+enum AMode { kAFrames = 0, kAImage = 1, kARows = 2 };
+
 // Launchers (pe_kernels.hip). Return the launch status.
-hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, hipStream_t st);
+// rows_map: pack bf16 in the patch-rows order instead of the temporal-split order
+hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, bool rows_map, hipStream_t st);
 hipError_t launch_bias(const void *b, int b_esz, float *bias32, int E, hipStream_t st);
 hipError_t launch_forward(const FwdArgs &a, int P, int in_esz, int out_esz, hipStream_t st);
 

@@ -68,7 +68,7 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float v) {
 // ----------------------------------------------------------------------------------------
 template <typename TW>
 __global__ void pe_pack_kernel(const TW *__restrict__ w, TW *__restrict__ wpk, int P, int E,
-                               int S) {
+                               int S, int rows_map) {
     constexpr int esz = sizeof(TW);
     constexpr int epf = 16 / esz;
     constexpr int NB = pack_block(esz);
@@ -85,6 +85,19 @@ __global__ void pe_pack_kernel(const TW *__restrict__ w, TW *__restrict__ wpk, i
     const int s = (int)(t / ncb);
     const int e = cb * NB + n;
     TW vals[epf];
+    if (esz == 2 && rows_map) {
+        // patch-rows map: elements [32s + 8g, +8) of the flattened (c, t, py, px) filter
+        const int K = kC * kTp * P * P;
+#pragma unroll
+        for (int j = 0; j < epf; ++j) {
+            const int k = 32 * s + 8 * g + j;
+            vals[j] = (e < E && k < K) ? w[(int64_t)e * K + k] : TW(0);
+        }
+        TW *dst = wpk + idx * epf;
+#pragma unroll
+        for (int j = 0; j < epf; ++j) dst[j] = vals[j];
+        return;
+    }
     if constexpr (esz == 2) {
         // temporal-split map: g = 2j + tt, unique fragment uf = 2s + j
         const int tt = g & 1;
@@ -198,6 +211,109 @@ __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ---- A fragments of the 32x32x16 kernels (temporal-split map, see pe_internal.h).
+// Byte offset of element x of pixel row u (u = c*P + py) of one temporal slot.
+template <int P>
+__device__ __forceinline__ uint32_t frag_off(int u, int x, uint32_t plane, uint32_t rstr) {
+    return ((uint32_t)(u / P) * plane + (uint32_t)(u % P) * rstr + (uint32_t)x) * 2u;
+}
+// Image launches (every item one frame): both temporal slots read the same pixels, so the two
+// lane halves of a k-step would load the same bytes twice. Instead one load brings unique fragment
+// uf = 2s to lanes 0-31 and uf = 2s + 1 to lanes 32-63, and v_permlane32_swap then copies each
+// into both halves: half the load instructions and half the bytes. This needs the two fragments
+// to be the same kind of load; P = 14's last step (a split fragment and the 8-byte tail) is not.
+template <int P, int s>
+__device__ constexpr bool img_paired() {
+    constexpr UFrag f0 = tt_frag(P, 2 * s), f1 = tt_frag(P, 2 * s + 1);
+    return f0.kind == f1.kind && f0.kind != kUfTail4;
+}
+// Issue the A loads of k-step s for TM 32-row blocks (vb: per-lane byte offset of the lane's
+// patch and temporal slot). Paired image steps leave their two fragments in dst[rb][0].
+template <int P, int TM, int AM, int s>
+__device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&vb)[TM],
+                                            uint32_t plane, uint32_t rstr, int h, u32x4 (&dst)[TM][2]) {
+    if constexpr (AM == kARows) {
+        // vb holds the row's byte offset plus 16 for lanes 32-63 (lane group g = 2j + h)
+        constexpr int K = kC * kTp * P * P;
+        static_for<2>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int k0 = 32 * s + 16 * j;  // first element of lane half 0
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb) {
+                if constexpr (k0 >= K) {
+                    dst[rb][j] = u32x4{0u, 0u, 0u, 0u};
+                } else {
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vb[rb], 2 * k0, 0);
+                    // lanes 32-63 of the last fragment would read past the row: zero (the packed
+                    // weight is zero there too, but the next row's values could be non-finite)
+                    if constexpr (k0 + 8 >= K) dst[rb][j] = h ? u32x4{0u, 0u, 0u, 0u} : v;
+                    else dst[rb][j] = v;
+                }
+            }
+        });
+    } else if constexpr (AM == kAImage && img_paired<P, s>()) {
+        constexpr UFrag f0 = tt_frag(P, 2 * s), f1 = tt_frag(P, 2 * s + 1);
+        const uint32_t o0 = frag_off<P>(f0.u1, f0.x1, plane, rstr);
+        const uint32_t hd = h ? frag_off<P>(f1.u1, f1.x1, plane, rstr) - o0 : 0u;
+        if constexpr (f0.kind == kUfFull) {
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb)
+                dst[rb][0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(vb[rb] + hd), (int)o0, 0);
+        } else {
+            const uint32_t p0 = frag_off<P>(f0.u2, f0.x2, plane, rstr);
+            const uint32_t hd2 = h ? frag_off<P>(f1.u2, f1.x2, plane, rstr) - p0 : 0u;
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb) {
+                const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, (int)(vb[rb] + hd), (int)o0, 0);
+                const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(vb[rb] + hd2), (int)p0, 0);
+                dst[rb][0] = u32x4{m3.x, m3.y, m3.z, e1};
+            }
+        }
+    } else {
+        static_for<2>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr UFrag f = tt_frag(P, 2 * s + j);
+            const int so1 = (int)frag_off<P>(f.u1, f.x1, plane, rstr);
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb) {
+                if constexpr (f.kind == kUfFull) {
+                    dst[rb][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vb[rb], so1, 0);
+                } else if constexpr (f.kind == kUfSplit62) {
+                    const int so2 = (int)frag_off<P>(f.u2, f.x2, plane, rstr);
+                    const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, (int)vb[rb], so1, 0);
+                    const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)vb[rb], so2, 0);
+                    dst[rb][j] = u32x4{m3.x, m3.y, m3.z, e1};
+                } else {
+                    const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)vb[rb], so1, 0);
+                    dst[rb][j] = u32x4{m2.x, m2.y, 0u, 0u};
+                }
+            }
+        });
+    }
+}
+// The matrix-core operands of k-step s from what load_a_step loaded: for a paired image step,
+// (lanes 0-31 of x, twice) and (lanes 32-63 of x, twice); otherwise the loads as they are.
+__device__ __forceinline__ void swap_halves(const u32x4 &x, u32x4 &lo, u32x4 &hi) {
+    const auto r0 = __builtin_amdgcn_permlane32_swap(x.x, x.x, false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(x.y, x.y, false, false);
+    const auto r2 = __builtin_amdgcn_permlane32_swap(x.z, x.z, false, false);
+    const auto r3 = __builtin_amdgcn_permlane32_swap(x.w, x.w, false, false);
+    lo = u32x4{r0[0], r1[0], r2[0], r3[0]};
+    hi = u32x4{r0[1], r1[1], r2[1], r3[1]};
+}
+template <int P, int TM, int AM, int s>
+__device__ __forceinline__ void a_operands(const u32x4 (&src)[TM][2], u32x4 (&dst)[TM][2]) {
+#pragma unroll
+    for (int rb = 0; rb < TM; ++rb) {
+        if constexpr (AM == kAImage && img_paired<P, s>()) {
+            swap_halves(src[rb][0], dst[rb][0], dst[rb][1]);
+        } else {
+            dst[rb][0] = src[rb][0];
+            dst[rb][1] = src[rb][1];
+        }
+    }
 }
 
 template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
@@ -434,13 +550,13 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs 
 // ----------------------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD>
+template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD, int AM>
 __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs a) {
     constexpr int ESZ = 2;
     constexpr int NT = WM * WN * 64;
     constexpr int BM = WM * TM * 32;
     constexpr int BN = WN * TN * 32;
-    constexpr int S = tt_steps(P);
+    constexpr int S = AM == kARows ? rows_steps(P) : tt_steps(P);
     constexpr int STAGE = BN * 64;                  // packed-weight bytes of one k-step
     constexpr int CH = (STAGE / 16 + NT - 1) / NT;  // 16-byte chunks per thread per k-step
     constexpr bool CH_EVEN = (STAGE / 16) % NT == 0;
@@ -471,14 +587,15 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     const int ncb = packed_cols(a.E, ESZ) >> 5;  // 32-column blocks of the packed weight
 
     // Per lane and 32-row block: byte offset of its patch's temporal slot h (the two lane halves
-    // read the two frames of the temporal patch: tstr = 0 for a repeated image frame). The
-    // per-step part of each address is the same for every row of the launch (one frame
-    // geometry per launch), so it is a scalar offset and the loads cost no vector arithmetic.
+    // read the two frames of the temporal patch: tstr = 0 for a repeated image frame), or for
+    // patch rows the row plus 8 elements for lanes 32-63. The per-step part of each address is the
+    // same for every row of the launch (one frame geometry per launch), so it is a scalar offset
+    // and the loads cost no vector arithmetic.
     uint32_t vb[TM];
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
         const PatchRef p = patch_of_row<P>(a, row0 + (wm * TM + rb) * 32 + l32);
-        vb[rb] = (p.base + (h ? p.tstr : 0u)) * 2u;
+        vb[rb] = AM == kARows ? p.base * 2u + (h ? 16u : 0u) : (p.base + (h ? p.tstr : 0u)) * 2u;
     }
 
     const __amdgpu_buffer_rsrc_t rsrc =
@@ -488,26 +605,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     // A fragments of k-step s (sub-steps j = 0, 1). Loads only; the data is first used by the
     // step's matrix products.
     auto load_a = [&](auto sc, u32x4 (&dst)[TM][2]) {
-        constexpr int s = decltype(sc)::value;
-        static_for<2>([&](auto jc) {
-            constexpr int j = decltype(jc)::value;
-            constexpr UFrag f = tt_frag(P, 2 * s + j);
-            const int so1 = (int)(((uint32_t)(f.u1 / P) * plane + (uint32_t)(f.u1 % P) * rstr + f.x1) * 2u);
-#pragma unroll
-            for (int rb = 0; rb < TM; ++rb) {
-                if constexpr (f.kind == kUfFull) {
-                    dst[rb][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vb[rb], so1, 0);
-                } else if constexpr (f.kind == kUfSplit62) {
-                    const int so2 = (int)(((uint32_t)(f.u2 / P) * plane + (uint32_t)(f.u2 % P) * rstr + f.x2) * 2u);
-                    const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, (int)vb[rb], so1, 0);
-                    const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)vb[rb], so2, 0);
-                    dst[rb][j] = u32x4{m3.x, m3.y, m3.z, e1};
-                } else {
-                    const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)vb[rb], so1, 0);
-                    dst[rb][j] = u32x4{m2.x, m2.y, 0u, 0u};
-                }
-            }
-        });
+        load_a_step<P, TM, AM, decltype(sc)::value>(rsrc, vb, plane, rstr, h, dst);
     };
 
     // Packed weight of k-step s for the tile's columns: BN*64 contiguous bytes. Chunks past the
@@ -548,8 +646,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         for (int rb = 0; rb < TM; ++rb) acc[rb][cb] = b16;
     }
 
-    auto compute = [&](auto sc, const u32x4 (&af)[TM][2]) {
+    auto compute = [&](auto sc, const u32x4 (&ald)[TM][2]) {
         constexpr int s = decltype(sc)::value;
+        u32x4 af[TM][2];
+        a_operands<P, TM, AM, s>(ald, af);
         // fragment (j, cb) of this step: 1 KB at stage + (wn*TN + cb)*2 KB + j*1 KB
         const u32x4 *bs = reinterpret_cast<const u32x4 *>(lds + ((s / KS) & 1) * KBUF + (s % KS) * STAGE) +
                           wn * TN * 128 + lane;
@@ -580,11 +680,16 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         }
     };
 
-    // ---- k loop, fully unrolled. A runs AD k-steps ahead in an (AD+1)-deep register ring. The
-    // packed weight sits in two LDS buffers of KS k-steps each (one barrier per KS k-steps);
-    // while the waves compute from one buffer they fill the other one k-step at a time from a
-    // BD-deep register ring (each weight k-step is loaded BD-1 k-steps before it is stored).
-    u32x4 Ar[AD + 1][TM][2], Br[BD][CH];
+    // ---- k loop, fully unrolled. A runs AD k-steps ahead in a register ring. Patch rows load
+    // A two k-steps at a time (the 128 bytes of each row that two k-steps read are one cache
+    // line, fetched once). The packed weight sits in two LDS buffers of KS k-steps each (one
+    // barrier per KS k-steps); while the waves compute from one buffer they fill the other one
+    // k-step at a time from a BD-deep register ring (each weight k-step is loaded BD-1 k-steps
+    // before it is stored).
+    constexpr bool PAIR = AM == kARows;
+    constexpr int RD = PAIR ? AD + 2 : AD + 1;           // A ring depth
+    constexpr int PRE = PAIR ? (AD + 1) / 2 * 2 : AD;    // A k-steps loaded before the loop
+    u32x4 Ar[RD][TM][2], Br[BD][CH];
     {
         u32x4 tmp[CH];
 #pragma unroll
@@ -597,14 +702,19 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         constexpr int t = KS + decltype(ic)::value;
         if constexpr (t < S) load_b(t, Br[t % BD]);
     });
-    static_for<(AD < S ? AD : S)>([&](auto jc) { load_a(jc, Ar[decltype(jc)::value]); });
+    static_for<(PRE < S ? PRE : S)>([&](auto jc) { load_a(jc, Ar[decltype(jc)::value]); });
     __syncthreads();
     static_for<S>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         constexpr int t = s + KS;
         if constexpr (t + BD - 1 < S) load_b(t + BD - 1, Br[(t + BD - 1) % BD]);
-        if constexpr (s + AD < S) load_a(IC<s + AD>{}, Ar[(s + AD) % (AD + 1)]);
-        compute(sc, Ar[s % (AD + 1)]);
+        if constexpr (!PAIR) {
+            if constexpr (s + AD < S) load_a(IC<s + AD>{}, Ar[(s + AD) % RD]);
+        } else if constexpr ((s + AD) % 2 == 0 && s + AD >= PRE) {
+            if constexpr (s + AD < S) load_a(IC<s + AD>{}, Ar[(s + AD) % RD]);
+            if constexpr (s + AD + 1 < S) load_a(IC<s + AD + 1>{}, Ar[(s + AD + 1) % RD]);
+        }
+        compute(sc, Ar[s % RD]);
         if constexpr (t < S) store_b(t, Br[t % BD]);
         if constexpr (s % KS == KS - 1 && s + 1 < S) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
@@ -670,11 +780,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 // go from global memory straight to registers, with no LDS stage and no barrier in the k loop.
 // The four fp32 partial tiles meet in LDS at the end and are summed in a fixed order.
 // ----------------------------------------------------------------------------------------
-template <int P, int OSZ, int TM, int TN, int AD>
+template <int P, int OSZ, int TM, int TN, int AD, int AM>
 __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     constexpr int NW = 4;
     constexpr int BM = TM * 32, BN = TN * 32;
-    constexpr int S = tt_steps(P);
+    constexpr int S = AM == kARows ? rows_steps(P) : tt_steps(P);
     constexpr int PITCH = BN + 8;                   // dwords per partial-tile row (8 mod 16)
     constexpr int PART = BM * PITCH * 4;            // bytes per wave's partial tile
     __shared__ __attribute__((aligned(16))) unsigned char lds[NW * PART];
@@ -699,7 +809,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
         const PatchRef p = patch_of_row<P>(a, row0 + rb * 32 + l32);
-        vb[rb] = (p.base + (h ? p.tstr : 0u)) * 2u;
+        vb[rb] = AM == kARows ? p.base * 2u + (h ? 16u : 0u) : (p.base + (h ? p.tstr : 0u)) * 2u;
     }
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.in), (short)0, (int)a.in_bytes, kBufWord3);
@@ -727,30 +837,17 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     struct Frags { u32x4 a[TM][2]; u32x4 b[TN][2]; };
     auto load = [&](auto sc, Frags &d) {
         constexpr int s = decltype(sc)::value;
+        load_a_step<P, TM, AM, s>(rsrc, vb, plane, rstr, h, d.a);
         static_for<2>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
-            constexpr UFrag f = tt_frag(P, 2 * s + j);
-            const int so1 = (int)(((uint32_t)(f.u1 / P) * plane + (uint32_t)(f.u1 % P) * rstr + f.x1) * 2u);
-#pragma unroll
-            for (int rb = 0; rb < TM; ++rb) {
-                if constexpr (f.kind == kUfFull) {
-                    d.a[rb][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vb[rb], so1, 0);
-                } else if constexpr (f.kind == kUfSplit62) {
-                    const int so2 = (int)(((uint32_t)(f.u2 / P) * plane + (uint32_t)(f.u2 % P) * rstr + f.x2) * 2u);
-                    const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, (int)vb[rb], so1, 0);
-                    const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)vb[rb], so2, 0);
-                    d.a[rb][j] = u32x4{m3.x, m3.y, m3.z, e1};
-                } else {
-                    const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)vb[rb], so1, 0);
-                    d.a[rb][j] = u32x4{m2.x, m2.y, 0u, 0u};
-                }
-            }
             const int sw = (int)(((uint32_t)s * (uint32_t)ncb * 2u + j) * 1024u);
 #pragma unroll
             for (int cb = 0; cb < TN; ++cb) d.b[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)wb[cb], sw, 0);
         });
     };
-    auto mma = [&](const Frags &d) {
+    auto mma = [&](auto sc, const Frags &d) {
+        u32x4 af[TM][2];
+        a_operands<P, TM, AM, decltype(sc)::value>(d.a, af);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -758,7 +855,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
 #pragma unroll
                 for (int rb = 0; rb < TM; ++rb)
                     acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, d.a[rb][j]), __builtin_bit_cast(bf16x8, d.b[cb][j]), acc[rb][cb], 0, 0, 0);
+                        __builtin_bit_cast(bf16x8, af[rb][j]), __builtin_bit_cast(bf16x8, d.b[cb][j]), acc[rb][cb], 0, 0, 0);
     };
     // wave W: k-steps [W*S/NW, (W+1)*S/NW), loads AD steps ahead in an (AD+1)-deep ring
     auto run = [&](auto wc) {
@@ -772,7 +869,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
         static_for<n>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i + AD < n) load(IC<lo + i + AD>{}, ring[(i + AD) % (AD + 1)]);
-            mma(ring[i % (AD + 1)]);
+            mma(IC<lo + i>{}, ring[i % (AD + 1)]);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -835,17 +932,17 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
 // ----------------------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------------------
-hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, hipStream_t st) {
+hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, bool rows_map, hipStream_t st) {
     const int S = packed_steps(P, w_esz);
     const int64_t total = (int64_t)S * packed_cols(E, w_esz) * 4;
     const int threads = 256;
     const int blocks = (int)((total + threads - 1) / threads);
     if (w_esz == 2)
         hipLaunchKernelGGL(pe_pack_kernel<uint16_t>, dim3(blocks), dim3(threads), 0, st,
-                           static_cast<const uint16_t *>(w), static_cast<uint16_t *>(wpk), P, E, S);
+                           static_cast<const uint16_t *>(w), static_cast<uint16_t *>(wpk), P, E, S, rows_map ? 1 : 0);
     else
         hipLaunchKernelGGL(pe_pack_kernel<float>, dim3(blocks), dim3(threads), 0, st,
-                           static_cast<const float *>(w), static_cast<float *>(wpk), P, E, S);
+                           static_cast<const float *>(w), static_cast<float *>(wpk), P, E, S, 0);
     return hipGetLastError();
 }
 
@@ -875,8 +972,13 @@ static hipError_t launch32(FwdArgs a, hipStream_t st) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
-    hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD, BD>), dim3(a.tiles_m * a.tiles_n),
-                       dim3(WM * WN * 64), 0, st, a);
+    const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+    if (a.kind == 0)
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kARows>), grid, block, 0, st, a);
+    else if (a.img)
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAImage>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAFrames>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -885,7 +987,13 @@ static hipError_t launch_sk(FwdArgs a, hipStream_t st) {
     constexpr int BM = TM * 32, BN = TN * 32;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
-    hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, OSZ, TM, TN, AD>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, st, a);
+    const dim3 grid(a.tiles_m * a.tiles_n), block(256);
+    if (a.kind == 0)
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, OSZ, TM, TN, AD, kARows>), grid, block, 0, st, a);
+    else if (a.img)
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, OSZ, TM, TN, AD, kAImage>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, OSZ, TM, TN, AD, kAFrames>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
