@@ -1005,9 +1005,11 @@ static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
         return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
     } else {
         // 256 x 256 tiles (8 waves of 32 x 256, two per SIMD) once there are enough of them to
-        // occupy about half the CUs. Measured on workloads of 1k, 8k and 332k patches.
+        // occupy about half the CUs; one weight k-step per LDS buffer (a barrier per k-step
+        // measured ~2% faster than two), eight weight fragments read ahead. Measured on
+        // workloads of 1k, 8k and 332k patches.
         const int64_t big = ((int64_t)(a.n_rows + 255) / 256) * ((a.E + 255) / 256);
-        if (big >= 128) return launch32<P, OSZ, 1, 8, 8, 1, 2, 4, 2, 3>(a, st);
+        if (big >= 128) return launch32<P, OSZ, 1, 8, 8, 1, 1, 8, 2, 3>(a, st);
         // few rows: split-K workgroups, 32 rows by 160 (or 128) columns
         if (a.E % 160 == 0) return launch_sk<P, OSZ, 1, 5, 2>(a, st);
         return launch_sk<P, OSZ, 1, 4, 2>(a, st);
