@@ -35,15 +35,16 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(wl):
+def algorithmic(wl, rows=False):
     """FLOPs and algorithmic HBM bytes of one step: unique input read once (one frame per image,
-    every frame of a video; patch rows as given), packed weight, bias, output."""
+    every frame of a video; patch rows as given), packed weight, bias, output. rows: the same
+    patches given as pre-flattened rows [N, K]."""
     import workloads
     esz = {"bf16": 2, "f32": 4}
     n = sum(t * h * w for (t, h, w) in wl.grid)
     flops = 2.0 * n * wl.k * wl.embed
     inp = 1
-    for d in wl.input_shape:
+    for d in (wl.input_shape if not rows else (n, wl.k)):
         inp *= d
     byts = inp * esz[wl.in_dtype] + wl.embed * wl.k * esz[wl.w_dtype] + \
         (wl.embed * esz[wl.w_dtype] if wl.bias else 0) + n * wl.embed * esz[wl.out_dtype]
@@ -63,7 +64,9 @@ def dominant_kernel(wl):
     return "pe_fwd32_kernel" if tiles >= 128 else "pe_fwd32_sk_kernel"
 
 
-def time_workload(idx, steps, warmup, graph=True):
+def time_workload(idx, steps, warmup, graph=True, rows=False):
+    """rows: feed the workload's patches as pre-flattened rows [N, K] (the processor's
+    pixel_values layout) instead of its frames: same N, weight and bias, synthetic N(0, 1) rows."""
     import torch
     import workloads
     import vlm_vision_patch_amd as pe
@@ -71,22 +74,26 @@ def time_workload(idx, steps, warmup, graph=True):
     wl = workloads.WORKLOADS[idx]
     dev = torch.device("cuda:0")
     x, w, b = workloads.generate(wl)
+    n, flops, byts = algorithmic(wl, rows)
+    kind = wl.kind
+    grid, frames = [list(g) for g in wl.grid], list(wl.frames) or None
+    if rows:
+        x = workloads.random_tensor((n, wl.k), seed=1000 + idx, dtype=workloads.DTYPES[wl.in_dtype])
+        kind, grid, frames = "patches", [[1, 1, n]], None
     x, w = x.to(dev), w.to(dev)
     b = b.to(dev) if b is not None else None
     mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype])
-    grid, frames = [list(g) for g in wl.grid], list(wl.frames) or None
-    n, flops, byts = algorithmic(wl)
     out = torch.empty((n, wl.embed), dtype=workloads.DTYPES[wl.out_dtype], device=dev)
     s = torch.cuda.Stream(device=dev)   # default priority
     with torch.cuda.stream(s):
         for _ in range(warmup):
-            mod(x, grid, frames, kind=wl.kind, out=out)
+            mod(x, grid, frames, kind=kind, out=out)
         # eager: K launches from Python
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(s)
         for _ in range(steps):
-            mod(x, grid, frames, kind=wl.kind, out=out)
+            mod(x, grid, frames, kind=kind, out=out)
         e1.record(s)
         torch.cuda.synchronize()
         eager_ms = e0.elapsed_time(e1) / steps
@@ -96,7 +103,7 @@ def time_workload(idx, steps, warmup, graph=True):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             for _ in range(steps):
-                mod(x, grid, frames, kind=wl.kind, out=out)
+                mod(x, grid, frames, kind=kind, out=out)
         with torch.cuda.stream(s):
             g.replay()                       # untimed: first replay uploads the graph
             torch.cuda.synchronize()
@@ -109,7 +116,7 @@ def time_workload(idx, steps, warmup, graph=True):
         timing = "K steps captured in one HIP graph, replayed once between HIP events"
         del g
     mod.close()
-    return dict(wl=wl, n=n, flops=flops, bytes=byts, ms=ms, eager_ms=eager_ms, timing=timing)
+    return dict(wl=wl, n=n, flops=flops, bytes=byts, ms=ms, eager_ms=eager_ms, timing=timing, rows=rows)
 
 
 def cpu_baseline(idx, min_seconds=10.0):
@@ -163,8 +170,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--extra", type=str, default="5",
-                    help="comma-separated further workloads reported under 'also' ('' for none)")
+    ap.add_argument("--extra", type=str, default="5,5r,4,1",
+                    help="comma-separated further workloads reported under 'also' ('' for none); "
+                         "a trailing r feeds that workload's patches as pre-flattened rows")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time K launches from Python instead of a captured graph (for counter runs)")
@@ -213,14 +221,15 @@ def main():
             "per_launch": {"flops": r["flops"], "alg_bytes": r["bytes"], "avg_us": round(r["ms"] * 1e3, 3)},
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     also = {}
-    for e in [int(v) for v in args.extra.split(",") if v.strip()]:
-        if e == args.workload:
+    for spec in [v.strip() for v in args.extra.split(",") if v.strip()]:
+        e, as_rows = int(spec.rstrip("r")), spec.endswith("r")
+        if e == args.workload and not as_rows:
             continue
         st = max(5, min(args.steps, 50))
-        q = time_workload(e, st, 3, graph=not args.eager)
+        q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows)
         qt = q["ms"] / 1e3
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
-        also[q["wl"].name] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
+        also[q["wl"].name + ("_as_patch_rows" if as_rows else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
                               "tflops": round(q["flops"] / qt / 1e12, 2),
                               "frac_matrix_peak": round(q["flops"] / qt / 1e12 / qpk, 4),
                               "frac_hbm": round(q["bytes"] / qt / 1e9 / PEAK_HBM_GBS, 4),
