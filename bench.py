@@ -51,17 +51,23 @@ def algorithmic(wl, rows=False):
     return n, flops, byts
 
 
-def dominant_kernel(wl):
-    """Name of the kernel that does the step's work. The library picks it per launch from the
-    launch's size: bf16 launches with at least 128 tiles of 256 x 256 outputs run the large-tile
-    kernel, smaller ones the split-k kernel; fp32 runs the 16x16 kernel. A frames launch holds at
-    most 64 items; the largest launch decides."""
+def dominant_kernel(wl, num_cus=256):
+    """Name of the kernel that does the step's work, by the library's tile choice for the largest
+    launch (a frames launch holds at most 64 items): in rounds of one workgroup per CU, 256 x 256
+    tiles cost ~30 us a round, 256 x 128 ~18 us and split-k ~8 us; the fewest (rounds x cost)
+    wins. fp32 runs the 16x16 kernel."""
     if wl.w_dtype != "bf16":
         return "pe_fwd16_kernel"
     rows = [t * h * w for (t, h, w) in wl.grid]
-    per_launch = max(sum(rows[i:i + 64]) for i in range(0, len(rows), 64))
-    tiles = ((per_launch + 255) // 256) * ((wl.embed + 255) // 256)
-    return "pe_fwd32_kernel" if tiles >= 128 else "pe_fwd32_sk_kernel"
+    n = max(sum(rows[i:i + 64]) for i in range(0, len(rows), 64))
+    E = wl.embed
+    rounds = lambda tiles: -(-tiles // num_cus)
+    rt = -(-n // 256)
+    skn = 160 if E % 160 == 0 else 128
+    c256 = rounds(rt * -(-E // 256)) * 30
+    c128 = rounds(rt * -(-E // 128)) * 18
+    csk = rounds(-(-n // 32) * -(-E // skn)) * 8
+    return "pe_fwd32_kernel" if min(c256, c128) <= csk else "pe_fwd32_sk_kernel"
 
 
 def time_workload(idx, steps, warmup, graph=True, rows=False):
@@ -209,7 +215,7 @@ def main():
     ai = r["flops"] / r["bytes"]
     ridge = peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9)
     bound = "mfma" if ai >= ridge else "hbm"
-    kname = dominant_kernel(wl)
+    kname = dominant_kernel(wl, torch.cuda.get_device_properties(0).multi_processor_count)
     traffic = load_traffic(kname, wl.name)
     roof = {"bound": bound,
             "achieved": round(tflops if bound == "mfma" else gbs, 3),

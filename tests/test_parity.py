@@ -173,6 +173,31 @@ def test_patch_rows(pe, P, N, dt, od):
     check(got, ref, od, "patches")
 
 
+@pytest.mark.parametrize("case", ["images_4x448_bias", "images_16x448", "rows_3000_E1168"])
+def test_mid_size_tiles(pe, case):
+    """Sizes where the launcher picks 256 x 128 tiles (between the split-k and the 256 x 256
+    ranges), including a ragged row count and an embed width that leaves a partial column block."""
+    if case.startswith("images"):
+        k = 4 if case == "images_4x448_bias" else 16
+        E, P = 1280, 14
+        K = 3 * 2 * P * P
+        x = make(700 + k, (k, 3, 448, 448), torch.bfloat16)
+        w = make(701, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+        b = make(702, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K)) if "bias" in case else None
+        grid, n = [[1, 32, 32]] * k, k * 1024
+        rows = sampled_rows(n, 11 + k, 400)
+        got, ref, od = run(pe, case, x, w, b, grid, [1] * k, order="merge", rows=rows)
+    else:
+        E, P, n = 1168, 14, 3000
+        K = 3 * 2 * P * P
+        x = make(710, (n, K), torch.bfloat16)
+        w = make(711, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+        b = make(712, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+        rows = sampled_rows(n, 13, 400)
+        got, ref, od = run(pe, case, x, w, b, [[1, 1, n]], kind="patches", rows=rows)
+    check(got, ref, od, case)
+
+
 def test_many_items_split_launches(pe):
     """More items than one launch's item table holds: the library splits the launches."""
     P, E = 14, 256

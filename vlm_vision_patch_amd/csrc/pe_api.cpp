@@ -16,6 +16,7 @@
 struct pe_handle_s {
     pe_config cfg;
     int device;
+    int num_cus;    // compute units of the device (tile-size choice)
     int steps;
     void *wpk;      // packed weight for frames, steps * packed_cols(E) * 64 bytes
     void *wpk_rows; // bf16: the same weight packed for patch rows (inside wpk's allocation); fp32: wpk
@@ -120,6 +121,11 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     if (!h) return fail(PE_ERR_OOM, "host allocation failed");
     h->cfg = *cfg;
     h->device = dev;
+    h->num_cus = 0;
+    if (hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        h->num_cus = 0;  // the tile choice then assumes 256
+        (void)hipGetLastError();
+    }
     h->steps = steps;
     h->wpk = nullptr;
     h->wpk_rows = nullptr;
@@ -223,6 +229,7 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
     memset(&a, 0, sizeof a);
     a.wpk = h->wpk;
     a.bias = h->bias32;
+    a.num_cus = h->num_cus;
     a.E = E;
     a.m = m;
     a.order = merge ? 1 : 0;

@@ -997,22 +997,40 @@ static hipError_t launch_sk(FwdArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Tile choice: the largest tile that still gives every CU work.
+// Tile choice. A launch runs in rounds of at most one workgroup per CU; the cost of a round was
+// measured per tile shape (bf16, P = 14, 1k to 332k patches): 256 x 256 tiles ~30 us, 256 x 128
+// ~18 us, split-k 32 x 160 ~8 us. The shape with the fewest (rounds x round cost) wins; ties go to
+// the larger tile (better per area when the chip is full).
+// returns 0: 256 x 256, 1: 256 x 128, 2: split-k
+__host__ inline int choose_tiles(int64_t n_rows, int E, int num_cus) {
+    const int64_t ncu = num_cus > 0 ? num_cus : 256;
+    auto rounds = [&](int64_t tiles) { return (tiles + ncu - 1) / ncu; };
+    const int64_t rt = (n_rows + 255) / 256;
+    const int skn = E % 160 == 0 ? 160 : 128;
+    const int64_t c256 = rounds(rt * ((E + 255) / 256)) * 30;
+    const int64_t c128 = rounds(rt * ((E + 127) / 128)) * 18;
+    const int64_t csk = rounds(((n_rows + 31) / 32) * ((E + skn - 1) / skn)) * 8;
+    if (c256 <= c128 && c256 <= csk) return 0;
+    if (c128 <= csk) return 1;
+    return 2;
+}
+
 template <int P, int ESZ, int OSZ>
 static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
     if constexpr (ESZ == 4) {
         // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps)
         return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
     } else {
-        // 256 x 256 tiles (8 waves of 32 x 256, two per SIMD) once there are enough of them to
-        // occupy about half the CUs; one weight k-step per LDS buffer (a barrier per k-step
-        // measured ~2% faster than two), eight weight fragments read ahead. Measured on
-        // workloads of 1k, 8k and 332k patches.
-        const int64_t big = ((int64_t)(a.n_rows + 255) / 256) * ((a.E + 255) / 256);
-        if (big >= 128) return launch32<P, OSZ, 1, 8, 8, 1, 1, 8, 2, 3>(a, st);
-        // few rows: split-K workgroups, 32 rows by 160 (or 128) columns
-        if (a.E % 160 == 0) return launch_sk<P, OSZ, 1, 5, 2>(a, st);
-        return launch_sk<P, OSZ, 1, 4, 2>(a, st);
+        // 8 waves of 32 x BN (two per SIMD), one weight k-step per LDS buffer (a barrier per k-step
+        // measured ~2% faster than two), eight weight fragments read ahead
+        switch (choose_tiles(a.n_rows, a.E, a.num_cus)) {
+            case 0: return launch32<P, OSZ, 1, 8, 8, 1, 1, 8, 2, 3>(a, st);
+            case 1: return launch32<P, OSZ, 1, 4, 8, 1, 1, 8, 2, 3>(a, st);
+            default:
+                // few rows: split-K workgroups, 32 rows by 160 (or 128) columns
+                if (a.E % 160 == 0) return launch_sk<P, OSZ, 1, 5, 2>(a, st);
+                return launch_sk<P, OSZ, 1, 4, 2>(a, st);
+        }
     }
 }
 
