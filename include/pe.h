@@ -93,7 +93,10 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
  *   h          handle from pe_create. Immutable: concurrent calls on different streams are safe.
  *   input_kind pe_input_kind (see above).
  *   input      device buffer (PATCHES: [N, K]; FRAMES: the items' frames back to back).
- *   in_dtype   pe_dtype of the input; must equal the handle's weight dtype.
+ *   in_dtype   pe_dtype of the input. With a bf16 weight: bf16, or fp32, which is rounded to bf16
+ *              (nearest-even) as it is loaded: the cast of the input to the weight dtype that the
+ *              Qwen3VLVisionPatchEmbed forward does ("Optimize VLM PatchEmbed"). With an fp32
+ *              weight: fp32.
  *   grid_thw   HOST int32 [n_items, 3]: per item (t, h, w) in patches; N = sum t*h*w.
  *   frames     HOST int32 [n_items] frame counts F_i for FRAMES input, or NULL: then an item
  *              with t = 1 is one image frame (F = 1) and an item with t > 1 has F = Tp*t.
@@ -106,9 +109,9 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
  * kernel launch covers up to 64 consecutive items of one frame size (h, w) that are all single
  * images (F = 1) or all not.
  * Returns PE_OK, PE_ERR_INVALID_ARG, PE_ERR_SHAPE (a non-positive t/h/w, F_i inconsistent
- * with t_i, merge order with h or w not divisible by m, N >= 2^31), PE_ERR_UNSUPPORTED (dtype
- * mismatch; one item's frames or one launch's patch rows beyond 4 GiB) or PE_ERR_HIP (launch
- * failure). Validation happens before any launch.
+ * with t_i, merge order with h or w not divisible by m, N >= 2^31), PE_ERR_UNSUPPORTED (bf16
+ * input on an fp32 weight; one item's frames or one launch's patch rows beyond 4 GiB) or
+ * PE_ERR_HIP (launch failure). Validation happens before any launch.
  */
 int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
                const int32_t *grid_thw, const int32_t *frames, int32_t n_items, void *out,

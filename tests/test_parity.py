@@ -59,7 +59,9 @@ def run(pe, name, x, w, b, grid, frames=None, kind="frames", order="raster", out
         got = out[torch.as_tensor(rows, device=DEV)].float().cpu().double().numpy()
     else:
         got = out.float().cpu().double().numpy()
-    ref = oracle.forward(x, w, b, grid=grid, frames=frames, kind=kind, order=order, rows=rows)
+    cast = None if x.dtype == w.dtype else {torch.bfloat16: "bf16", torch.float32: "f32"}[w.dtype]
+    ref = oracle.forward(x, w, b, grid=grid, frames=frames, kind=kind, order=order, rows=rows,
+                         cast_input_to=cast)
     mod.close()
     return got, ref, out_dtype
 
@@ -198,6 +200,41 @@ def test_mid_size_tiles(pe, case):
     check(got, ref, od, case)
 
 
+@pytest.mark.parametrize("case", ["image_small_merge", "video_odd_frames", "images_mid", "images_8",
+                                  "rows_small", "rows_large", "image_p16_bias"])
+def test_fp32_input_bf16_weight(pe, case):
+    """fp32 pixels on a bf16 weight: rounded to bf16 (nearest even) on load, as the module's
+    input cast does; the oracle rounds the input the same way first."""
+    P = 16 if "p16" in case else 14
+    K = 3 * 2 * P * P
+    E = 1152 if "p16" in case else 1280
+    w = make(801, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(802, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K)) if "bias" in case or "video" in case else None
+    rows = None
+    if case.startswith("rows"):
+        n = 300 if case == "rows_small" else 20000
+        x = make(803 + n, (n, K), torch.float32)
+        rows = None if n <= 4000 else sampled_rows(n, 17, 400)
+        got, ref, od = run(pe, case, x, w, b, [[1, 1, n]], kind="patches", out_dtype=torch.bfloat16, rows=rows)
+    else:
+        if case == "image_small_merge":
+            items = [(1, 16, 20, 1)]
+        elif case == "video_odd_frames":
+            items = [(2, 8, 6, 3), (1, 4, 4, 2)]
+        elif case == "image_p16_bias":
+            items = [(1, 28, 28, 1)]
+        else:
+            items = [(1, 32, 32, 1)] * (4 if case == "images_mid" else 8)
+        x = torch.cat([make(810 + i, (F, 3, hh * P, ww * P), torch.float32).reshape(-1)
+                       for i, (t, hh, ww, F) in enumerate(items)])
+        grid = [[t, hh, ww] for (t, hh, ww, F) in items]
+        n = sum(t * hh * ww for (t, hh, ww) in grid)
+        rows = None if n <= 4000 else sampled_rows(n, 19, 400)
+        got, ref, od = run(pe, case, x, w, b, grid, [F for (*_, F) in items], order="merge",
+                           out_dtype=torch.bfloat16, rows=rows)
+    check(got, ref, od, case)
+
+
 def test_many_items_split_launches(pe):
     """More items than one launch's item table holds: the library splits the launches."""
     P, E = 14, 256
@@ -262,7 +299,13 @@ def test_forward_error_paths(pe):
     h = mod._h
     g = lambda *v: (ctypes.c_int32 * len(v))(*v)
     X, O = 0x1000, 0x2000   # never dereferenced: every call below fails validation first
-    assert pe.lib.pe_forward(h, 1, X, 0, g(1, 2, 2), None, 1, O, None) == pe.PE_ERR_UNSUPPORTED  # dtype
+    # bf16 input on an fp32 weight is the unsupported dtype pair (fp32 input on a bf16 weight is
+    # supported, so it must not be called with these fake pointers)
+    w32 = make(503, (64, 3, 2, 14, 14), torch.float32).to(DEV)
+    mod32 = pe.PatchEmbed(w32, order="merge")
+    assert pe.lib.pe_forward(mod32._h, 1, X, 1, g(1, 2, 2), None, 1, O, None) == pe.PE_ERR_UNSUPPORTED
+    assert "supported are" in pe.last_error()
+    mod32.close()
     assert pe.lib.pe_forward(h, 1, X, 1, g(1, 2, 3), None, 1, O, None) == pe.PE_ERR_SHAPE        # odd w
     assert pe.lib.pe_forward(h, 1, X, 1, g(1, 2, 2), g(3), 1, O, None) == pe.PE_ERR_SHAPE        # F vs t
     assert pe.lib.pe_forward(h, 1, X, 1, g(1, -2, 2), None, 1, O, None) == pe.PE_ERR_SHAPE

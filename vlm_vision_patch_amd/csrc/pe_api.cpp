@@ -187,11 +187,13 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         return fail(PE_ERR_INVALID_ARG, "bad input_kind %d", input_kind);
     if (!dtype_ok(in_dtype)) return fail(PE_ERR_INVALID_ARG, "bad in_dtype %d", in_dtype);
     const pe_config &cfg = h->cfg;
-    if (in_dtype != cfg.weight_dtype)
-        return fail(PE_ERR_UNSUPPORTED, "in_dtype %d differs from the weight dtype %d", in_dtype, cfg.weight_dtype);
+    // bf16 weight: bf16 input, or fp32 input rounded to bf16 on load; fp32 weight: fp32 input
+    if (in_dtype != cfg.weight_dtype && !(cfg.weight_dtype == PE_BF16 && in_dtype == PE_F32))
+        return fail(PE_ERR_UNSUPPORTED, "in_dtype %d with weight dtype %d: supported are bf16/bf16, "
+                    "fp32/bf16 (rounded on load) and fp32/fp32", in_dtype, cfg.weight_dtype);
 
     const int P = cfg.patch_size, E = cfg.embed_dim, m = cfg.spatial_merge_size;
-    const int ies = esize(in_dtype), oes = esize(cfg.out_dtype);
+    const int ies = esize(in_dtype), oes = esize(cfg.out_dtype), wes = esize(cfg.weight_dtype);
     const int64_t K = (int64_t)pe::kC * pe::kTp * P * P;
     const bool merge = input_kind == PE_INPUT_FRAMES && cfg.out_order == PE_ORDER_MERGE_WINDOW;
 
@@ -249,7 +251,7 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
             a.n_rows = (int32_t)nr;
             a.n_items = 0;
             a.colmajor = (uint64_t)nr * K * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
-            hipError_t e = pe::launch_forward(a, P, ies, oes, st);
+            hipError_t e = pe::launch_forward(a, P, wes, ies, oes, st);
             if (e != hipSuccess) return hip_fail(e, "forward launch");
         }
         return PE_OK;
@@ -292,7 +294,7 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
             it.x_off = (uint32_t)off;
             off += elems[i];
         }
-        hipError_t e = pe::launch_forward(a, P, ies, oes, st);
+        hipError_t e = pe::launch_forward(a, P, wes, ies, oes, st);
         if (e != hipSuccess) return hip_fail(e, "forward launch");
         x0 += span;
         i0 = i1;

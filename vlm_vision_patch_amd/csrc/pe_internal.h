@@ -173,6 +173,6 @@ enum AMode { kAFrames = 0, kAImage = 1, kARows = 2 };
 // rows_map: pack bf16 in the patch-rows order instead of the temporal-split order
 hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, bool rows_map, hipStream_t st);
 hipError_t launch_bias(const void *b, int b_esz, float *bias32, int E, hipStream_t st);
-hipError_t launch_forward(const FwdArgs &a, int P, int in_esz, int out_esz, hipStream_t st);
+hipError_t launch_forward(const FwdArgs &a, int P, int w_esz, int in_esz, int out_esz, hipStream_t st);
 
 }  // namespace pe

@@ -214,10 +214,62 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 // ---- A fragments of the 32x32x16 kernels (temporal-split map, see pe_internal.h).
+// The input is bf16 (ISZ = 2) or fp32 (ISZ = 4; rounded to bf16, nearest-even, when the products
+// use it). A fragment as loaded: one 16-byte register of 8 bf16, or two of 8 fp32.
+template <int ISZ> struct AFrag { u32x4 d[ISZ / 2]; };
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+template <int ISZ>
+__device__ __forceinline__ u32x4 frag_bf16(const AFrag<ISZ> &f) {
+    if constexpr (ISZ == 2) {
+        return f.d[0];
+    } else {
+        const f32x4 a = __builtin_bit_cast(f32x4, f.d[0]), b = __builtin_bit_cast(f32x4, f.d[1]);
+        return u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
+    }
+}
+// loads of 8 consecutive elements; of 6 + 2 elements from two places; of 4 elements + 4 zeros
+template <int ISZ>
+__device__ __forceinline__ void ld_whole(__amdgpu_buffer_rsrc_t r, uint32_t v, int so, AFrag<ISZ> &f) {
+    f.d[0] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, so, 0);
+    if constexpr (ISZ == 4) f.d[1] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, so + 16, 0);
+}
+template <int ISZ>
+__device__ __forceinline__ void ld_split62(__amdgpu_buffer_rsrc_t r, uint32_t v1, int so1, uint32_t v2, int so2,
+                                           AFrag<ISZ> &f) {
+    if constexpr (ISZ == 2) {
+        const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(r, (int)v1, so1, 0);
+        const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(r, (int)v2, so2, 0);
+        f.d[0] = u32x4{m3.x, m3.y, m3.z, e1};
+    } else {
+        f.d[0] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)v1, so1, 0);
+        const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(r, (int)v1, so1 + 16, 0);
+        const u32x2 e2 = __builtin_amdgcn_raw_buffer_load_b64(r, (int)v2, so2, 0);
+        f.d[1] = u32x4{m2.x, m2.y, e2.x, e2.y};
+    }
+}
+template <int ISZ>
+__device__ __forceinline__ void ld_tail4(__amdgpu_buffer_rsrc_t r, uint32_t v, int so, AFrag<ISZ> &f) {
+    if constexpr (ISZ == 2) {
+        const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(r, (int)v, so, 0);
+        f.d[0] = u32x4{m2.x, m2.y, 0u, 0u};
+    } else {
+        f.d[0] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, so, 0);
+        f.d[1] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+template <int ISZ>
+__device__ __forceinline__ void zero_frag(AFrag<ISZ> &f) {
+#pragma unroll
+    for (int i = 0; i < ISZ / 2; ++i) f.d[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // Byte offset of element x of pixel row u (u = c*P + py) of one temporal slot.
-template <int P>
+template <int P, int ISZ>
 __device__ __forceinline__ uint32_t frag_off(int u, int x, uint32_t plane, uint32_t rstr) {
-    return ((uint32_t)(u / P) * plane + (uint32_t)(u % P) * rstr + (uint32_t)x) * 2u;
+    return ((uint32_t)(u / P) * plane + (uint32_t)(u % P) * rstr + (uint32_t)x) * (uint32_t)ISZ;
 }
 // Image launches (every item one frame): both temporal slots read the same pixels, so the two
 // lane halves of a k-step would load the same bytes twice. Instead one load brings unique fragment
@@ -230,12 +282,12 @@ __device__ constexpr bool img_paired() {
     return f0.kind == f1.kind && f0.kind != kUfTail4;
 }
 // Issue the A loads of k-step s for TM 32-row blocks (vb: per-lane byte offset of the lane's
-// patch and temporal slot). Paired image steps leave their two fragments in dst[rb][0].
-template <int P, int TM, int AM, int s>
+// patch and temporal slot, or of its patch row plus 8 elements for lanes 32-63). Paired image
+// steps leave their two fragments in dst[rb][0].
+template <int P, int TM, int AM, int ISZ, int s>
 __device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&vb)[TM],
-                                            uint32_t plane, uint32_t rstr, int h, u32x4 (&dst)[TM][2]) {
+                                            uint32_t plane, uint32_t rstr, int h, AFrag<ISZ> (&dst)[TM][2]) {
     if constexpr (AM == kARows) {
-        // vb holds the row's byte offset plus 16 for lanes 32-63 (lane group g = 2j + h)
         constexpr int K = kC * kTp * P * P;
         static_for<2>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
@@ -243,58 +295,53 @@ __device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const u
 #pragma unroll
             for (int rb = 0; rb < TM; ++rb) {
                 if constexpr (k0 >= K) {
-                    dst[rb][j] = u32x4{0u, 0u, 0u, 0u};
+                    zero_frag(dst[rb][j]);
                 } else {
-                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vb[rb], 2 * k0, 0);
+                    ld_whole<ISZ>(rsrc, vb[rb], ISZ * k0, dst[rb][j]);
                     // lanes 32-63 of the last fragment would read past the row: zero (the packed
                     // weight is zero there too, but the next row's values could be non-finite)
-                    if constexpr (k0 + 8 >= K) dst[rb][j] = h ? u32x4{0u, 0u, 0u, 0u} : v;
-                    else dst[rb][j] = v;
+                    if constexpr (k0 + 8 >= K) {
+                        if (h) zero_frag(dst[rb][j]);
+                    }
                 }
             }
         });
     } else if constexpr (AM == kAImage && img_paired<P, s>()) {
         constexpr UFrag f0 = tt_frag(P, 2 * s), f1 = tt_frag(P, 2 * s + 1);
-        const uint32_t o0 = frag_off<P>(f0.u1, f0.x1, plane, rstr);
-        const uint32_t hd = h ? frag_off<P>(f1.u1, f1.x1, plane, rstr) - o0 : 0u;
+        const uint32_t o0 = frag_off<P, ISZ>(f0.u1, f0.x1, plane, rstr);
+        const uint32_t hd = h ? frag_off<P, ISZ>(f1.u1, f1.x1, plane, rstr) - o0 : 0u;
         if constexpr (f0.kind == kUfFull) {
 #pragma unroll
-            for (int rb = 0; rb < TM; ++rb)
-                dst[rb][0] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(vb[rb] + hd), (int)o0, 0);
+            for (int rb = 0; rb < TM; ++rb) ld_whole<ISZ>(rsrc, vb[rb] + hd, (int)o0, dst[rb][0]);
         } else {
-            const uint32_t p0 = frag_off<P>(f0.u2, f0.x2, plane, rstr);
-            const uint32_t hd2 = h ? frag_off<P>(f1.u2, f1.x2, plane, rstr) - p0 : 0u;
+            const uint32_t p0 = frag_off<P, ISZ>(f0.u2, f0.x2, plane, rstr);
+            const uint32_t hd2 = h ? frag_off<P, ISZ>(f1.u2, f1.x2, plane, rstr) - p0 : 0u;
 #pragma unroll
-            for (int rb = 0; rb < TM; ++rb) {
-                const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, (int)(vb[rb] + hd), (int)o0, 0);
-                const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(vb[rb] + hd2), (int)p0, 0);
-                dst[rb][0] = u32x4{m3.x, m3.y, m3.z, e1};
-            }
+            for (int rb = 0; rb < TM; ++rb)
+                ld_split62<ISZ>(rsrc, vb[rb] + hd, (int)o0, vb[rb] + hd2, (int)p0, dst[rb][0]);
         }
     } else {
         static_for<2>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             constexpr UFrag f = tt_frag(P, 2 * s + j);
-            const int so1 = (int)frag_off<P>(f.u1, f.x1, plane, rstr);
+            const int so1 = (int)frag_off<P, ISZ>(f.u1, f.x1, plane, rstr);
 #pragma unroll
             for (int rb = 0; rb < TM; ++rb) {
                 if constexpr (f.kind == kUfFull) {
-                    dst[rb][j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vb[rb], so1, 0);
+                    ld_whole<ISZ>(rsrc, vb[rb], so1, dst[rb][j]);
                 } else if constexpr (f.kind == kUfSplit62) {
-                    const int so2 = (int)frag_off<P>(f.u2, f.x2, plane, rstr);
-                    const u32x3 m3 = __builtin_amdgcn_raw_buffer_load_b96(rsrc, (int)vb[rb], so1, 0);
-                    const uint32_t e1 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)vb[rb], so2, 0);
-                    dst[rb][j] = u32x4{m3.x, m3.y, m3.z, e1};
+                    const int so2 = (int)frag_off<P, ISZ>(f.u2, f.x2, plane, rstr);
+                    ld_split62<ISZ>(rsrc, vb[rb], so1, vb[rb], so2, dst[rb][j]);
                 } else {
-                    const u32x2 m2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)vb[rb], so1, 0);
-                    dst[rb][j] = u32x4{m2.x, m2.y, 0u, 0u};
+                    ld_tail4<ISZ>(rsrc, vb[rb], so1, dst[rb][j]);
                 }
             }
         });
     }
 }
-// The matrix-core operands of k-step s from what load_a_step loaded: for a paired image step,
-// (lanes 0-31 of x, twice) and (lanes 32-63 of x, twice); otherwise the loads as they are.
+// The matrix-core operands of k-step s from what load_a_step loaded (rounded to bf16 here, where
+// they are used, so a load's wait is not pulled forward): for a paired image step, (lanes 0-31 of
+// x, twice) and (lanes 32-63 of x, twice); otherwise the loads as they are.
 __device__ __forceinline__ void swap_halves(const u32x4 &x, u32x4 &lo, u32x4 &hi) {
     const auto r0 = __builtin_amdgcn_permlane32_swap(x.x, x.x, false, false);
     const auto r1 = __builtin_amdgcn_permlane32_swap(x.y, x.y, false, false);
@@ -303,15 +350,15 @@ __device__ __forceinline__ void swap_halves(const u32x4 &x, u32x4 &lo, u32x4 &hi
     lo = u32x4{r0[0], r1[0], r2[0], r3[0]};
     hi = u32x4{r0[1], r1[1], r2[1], r3[1]};
 }
-template <int P, int TM, int AM, int s>
-__device__ __forceinline__ void a_operands(const u32x4 (&src)[TM][2], u32x4 (&dst)[TM][2]) {
+template <int P, int TM, int AM, int ISZ, int s>
+__device__ __forceinline__ void a_operands(const AFrag<ISZ> (&src)[TM][2], u32x4 (&dst)[TM][2]) {
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
         if constexpr (AM == kAImage && img_paired<P, s>()) {
-            swap_halves(src[rb][0], dst[rb][0], dst[rb][1]);
+            swap_halves(frag_bf16<ISZ>(src[rb][0]), dst[rb][0], dst[rb][1]);
         } else {
-            dst[rb][0] = src[rb][0];
-            dst[rb][1] = src[rb][1];
+            dst[rb][0] = frag_bf16<ISZ>(src[rb][0]);
+            dst[rb][1] = frag_bf16<ISZ>(src[rb][1]);
         }
     }
 }
@@ -550,7 +597,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs 
 // ----------------------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD, int AM>
+template <int P, int ISZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD, int AM>
 __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs a) {
     constexpr int ESZ = 2;
     constexpr int NT = WM * WN * 64;
@@ -595,7 +642,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
         const PatchRef p = patch_of_row<P>(a, row0 + (wm * TM + rb) * 32 + l32);
-        vb[rb] = AM == kARows ? p.base * 2u + (h ? 16u : 0u) : (p.base + (h ? p.tstr : 0u)) * 2u;
+        vb[rb] = AM == kARows ? (p.base + (h ? 8u : 0u)) * (uint32_t)ISZ : (p.base + (h ? p.tstr : 0u)) * (uint32_t)ISZ;
     }
 
     const __amdgpu_buffer_rsrc_t rsrc =
@@ -604,8 +651,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 
     // A fragments of k-step s (sub-steps j = 0, 1). Loads only; the data is first used by the
     // step's matrix products.
-    auto load_a = [&](auto sc, u32x4 (&dst)[TM][2]) {
-        load_a_step<P, TM, AM, decltype(sc)::value>(rsrc, vb, plane, rstr, h, dst);
+    auto load_a = [&](auto sc, AFrag<ISZ> (&dst)[TM][2]) {
+        load_a_step<P, TM, AM, ISZ, decltype(sc)::value>(rsrc, vb, plane, rstr, h, dst);
     };
 
     // Packed weight of k-step s for the tile's columns: BN*64 contiguous bytes. Chunks past the
@@ -646,10 +693,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         for (int rb = 0; rb < TM; ++rb) acc[rb][cb] = b16;
     }
 
-    auto compute = [&](auto sc, const u32x4 (&ald)[TM][2]) {
+    auto compute = [&](auto sc, const AFrag<ISZ> (&ald)[TM][2]) {
         constexpr int s = decltype(sc)::value;
         u32x4 af[TM][2];
-        a_operands<P, TM, AM, s>(ald, af);
+        a_operands<P, TM, AM, ISZ, s>(ald, af);
         // fragment (j, cb) of this step: 1 KB at stage + (wn*TN + cb)*2 KB + j*1 KB
         const u32x4 *bs = reinterpret_cast<const u32x4 *>(lds + ((s / KS) & 1) * KBUF + (s % KS) * STAGE) +
                           wn * TN * 128 + lane;
@@ -689,7 +736,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     constexpr bool PAIR = AM == kARows;
     constexpr int RD = PAIR ? AD + 2 : AD + 1;           // A ring depth
     constexpr int PRE = PAIR ? (AD + 1) / 2 * 2 : AD;    // A k-steps loaded before the loop
-    u32x4 Ar[RD][TM][2], Br[BD][CH];
+    AFrag<ISZ> Ar[RD][TM][2];
+    u32x4 Br[BD][CH];
     {
         u32x4 tmp[CH];
 #pragma unroll
@@ -780,7 +828,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 // go from global memory straight to registers, with no LDS stage and no barrier in the k loop.
 // The four fp32 partial tiles meet in LDS at the end and are summed in a fixed order.
 // ----------------------------------------------------------------------------------------
-template <int P, int OSZ, int TM, int TN, int AD, int AM>
+template <int P, int ISZ, int OSZ, int TM, int TN, int AD, int AM>
 __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     constexpr int NW = 4;
     constexpr int BM = TM * 32, BN = TN * 32;
@@ -809,7 +857,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
         const PatchRef p = patch_of_row<P>(a, row0 + rb * 32 + l32);
-        vb[rb] = AM == kARows ? p.base * 2u + (h ? 16u : 0u) : (p.base + (h ? p.tstr : 0u)) * 2u;
+        vb[rb] = AM == kARows ? (p.base + (h ? 8u : 0u)) * (uint32_t)ISZ : (p.base + (h ? p.tstr : 0u)) * (uint32_t)ISZ;
     }
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.in), (short)0, (int)a.in_bytes, kBufWord3);
@@ -834,10 +882,10 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
         for (int rb = 0; rb < TM; ++rb) acc[rb][cb] = b16;
     }
 
-    struct Frags { u32x4 a[TM][2]; u32x4 b[TN][2]; };
+    struct Frags { AFrag<ISZ> a[TM][2]; u32x4 b[TN][2]; };
     auto load = [&](auto sc, Frags &d) {
         constexpr int s = decltype(sc)::value;
-        load_a_step<P, TM, AM, s>(rsrc, vb, plane, rstr, h, d.a);
+        load_a_step<P, TM, AM, ISZ, s>(rsrc, vb, plane, rstr, h, d.a);
         static_for<2>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             const int sw = (int)(((uint32_t)s * (uint32_t)ncb * 2u + j) * 1024u);
@@ -847,7 +895,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     };
     auto mma = [&](auto sc, const Frags &d) {
         u32x4 af[TM][2];
-        a_operands<P, TM, AM, decltype(sc)::value>(d.a, af);
+        a_operands<P, TM, AM, ISZ, decltype(sc)::value>(d.a, af);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -967,33 +1015,33 @@ static hipError_t launch16(FwdArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int P, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD>
+template <int P, int ISZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD>
 static hipError_t launch32(FwdArgs a, hipStream_t st) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
     if (a.kind == 0)
-        hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kARows>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kARows>), grid, block, 0, st, a);
     else if (a.img)
-        hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAImage>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAImage>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((pe_fwd32_kernel<P, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAFrames>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAFrames>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
-template <int P, int OSZ, int TM, int TN, int AD>
+template <int P, int ISZ, int OSZ, int TM, int TN, int AD>
 static hipError_t launch_sk(FwdArgs a, hipStream_t st) {
     constexpr int BM = TM * 32, BN = TN * 32;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n), block(256);
     if (a.kind == 0)
-        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, OSZ, TM, TN, AD, kARows>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kARows>), grid, block, 0, st, a);
     else if (a.img)
-        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, OSZ, TM, TN, AD, kAImage>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAImage>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, OSZ, TM, TN, AD, kAFrames>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAFrames>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -1015,7 +1063,9 @@ __host__ inline int choose_tiles(int64_t n_rows, int E, int num_cus) {
     return 2;
 }
 
-template <int P, int ESZ, int OSZ>
+// ESZ: weight element size; ISZ: input element size (fp32 input meets a bf16 weight by rounding
+// on load)
+template <int P, int ESZ, int ISZ, int OSZ>
 static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
     if constexpr (ESZ == 4) {
         // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps)
@@ -1024,23 +1074,28 @@ static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
         // 8 waves of 32 x BN (two per SIMD), one weight k-step per LDS buffer (a barrier per k-step
         // measured ~2% faster than two), eight weight fragments read ahead
         switch (choose_tiles(a.n_rows, a.E, a.num_cus)) {
-            case 0: return launch32<P, OSZ, 1, 8, 8, 1, 1, 8, 2, 3>(a, st);
-            case 1: return launch32<P, OSZ, 1, 4, 8, 1, 1, 8, 2, 3>(a, st);
+            case 0: return launch32<P, ISZ, OSZ, 1, 8, 8, 1, 1, 8, 2, 3>(a, st);
+            case 1: return launch32<P, ISZ, OSZ, 1, 4, 8, 1, 1, 8, 2, 3>(a, st);
             default:
                 // few rows: split-K workgroups, 32 rows by 160 (or 128) columns
-                if (a.E % 160 == 0) return launch_sk<P, OSZ, 1, 5, 2>(a, st);
-                return launch_sk<P, OSZ, 1, 4, 2>(a, st);
+                if (a.E % 160 == 0) return launch_sk<P, ISZ, OSZ, 1, 5, 2>(a, st);
+                return launch_sk<P, ISZ, OSZ, 1, 4, 2>(a, st);
         }
     }
 }
 
-hipError_t launch_forward(const FwdArgs &a, int P, int in_esz, int out_esz, hipStream_t st) {
-    if (P == 14) {
-        if (in_esz == 2) return out_esz == 2 ? launch_p<14, 2, 2>(a, st) : launch_p<14, 2, 4>(a, st);
-        return out_esz == 2 ? launch_p<14, 4, 2>(a, st) : launch_p<14, 4, 4>(a, st);
+hipError_t launch_forward(const FwdArgs &a, int P, int w_esz, int in_esz, int out_esz, hipStream_t st) {
+    if (w_esz == 4) {  // fp32 weight: fp32 input
+        if (in_esz != 4) return hipErrorInvalidValue;
+        if (P == 14) return out_esz == 2 ? launch_p<14, 4, 4, 2>(a, st) : launch_p<14, 4, 4, 4>(a, st);
+        return out_esz == 2 ? launch_p<16, 4, 4, 2>(a, st) : launch_p<16, 4, 4, 4>(a, st);
     }
-    if (in_esz == 2) return out_esz == 2 ? launch_p<16, 2, 2>(a, st) : launch_p<16, 2, 4>(a, st);
-    return out_esz == 2 ? launch_p<16, 4, 2>(a, st) : launch_p<16, 4, 4>(a, st);
+    if (P == 14) {
+        if (in_esz == 2) return out_esz == 2 ? launch_p<14, 2, 2, 2>(a, st) : launch_p<14, 2, 2, 4>(a, st);
+        return out_esz == 2 ? launch_p<14, 2, 4, 2>(a, st) : launch_p<14, 2, 4, 4>(a, st);
+    }
+    if (in_esz == 2) return out_esz == 2 ? launch_p<16, 2, 2, 2>(a, st) : launch_p<16, 2, 2, 4>(a, st);
+    return out_esz == 2 ? launch_p<16, 2, 4, 2>(a, st) : launch_p<16, 2, 4, 4>(a, st);
 }
 
 }  // namespace pe
