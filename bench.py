@@ -10,6 +10,7 @@ stream they run on; `eager_ms_per_step` gives the same K steps launched one by o
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
@@ -24,8 +25,7 @@ METRIC = "PatchEmbed patches/s + TFLOP/s (% bf16 MFMA peak) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_F32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = [os.path.join(ROOT, "vlm_vision_patch_amd", "csrc", f)
-                  for f in ("pe_kernels.hip", "pe_internal.h", "pe_api.cpp")]
+KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "vlm_vision_patch_amd", "csrc", "*")))
 
 
 def kernel_hash() -> str:

@@ -1,5 +1,6 @@
 // pe_internal.h -- types shared by the C ABI (pe_api.cpp) and the gfx950 kernels
-// (pe_kernels.hip). Not installed; the public interface is include/pe.h.
+// (pe_kernels.h and the .hip units that instantiate it). Not installed; the public interface is
+// include/pe.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -169,10 +170,15 @@ __host__ __device__ constexpr int packed_steps(int P, int esz) {
 // (both slots the same pixels), or pre-flattened patch rows (the rows map above).
 enum AMode { kAFrames = 0, kAImage = 1, kARows = 2 };
 
-// Launchers (pe_kernels.hip). Return the launch status.
+// Launchers (pe_pack.hip and pe_fwd_p*.hip). Return the launch status.
 // rows_map: pack bf16 in the patch-rows order instead of the temporal-split order
 hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, bool rows_map, hipStream_t st);
 hipError_t launch_bias(const void *b, int b_esz, float *bias32, int E, hipStream_t st);
 hipError_t launch_forward(const FwdArgs &a, int P, int w_esz, int in_esz, int out_esz, hipStream_t st);
+// the forward kernels, one translation unit per patch size and input dtype (pe_fwd_p*.hip)
+hipError_t launch_forward_p14_bf16in(const FwdArgs &a, int out_esz, hipStream_t st);
+hipError_t launch_forward_p16_bf16in(const FwdArgs &a, int out_esz, hipStream_t st);
+hipError_t launch_forward_p14_f32in(const FwdArgs &a, int w_esz, int out_esz, hipStream_t st);
+hipError_t launch_forward_p16_f32in(const FwdArgs &a, int w_esz, int out_esz, hipStream_t st);
 
 }  // namespace pe

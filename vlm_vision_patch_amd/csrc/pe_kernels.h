@@ -1,4 +1,7 @@
-// pe_kernels.hip -- gfx950 kernels of the vision PatchEmbed.
+// pe_kernels.h -- gfx950 kernels of the vision PatchEmbed (templates). Included by the
+// translation units that instantiate them: pe_pack.hip (weight pack, bias, dispatch) and
+// pe_fwd_p{14,16}_{bf16,f32}in.hip (the forward kernels per patch size and input dtype),
+// which build in parallel.
 //
 // The operation ("Qwen2.5VL-Vision Encode-PatchEmbed", the bullet list on the convolution):
 // a Conv3d whose kernel equals its stride meets each patch once, so it is a matrix product
@@ -32,6 +35,8 @@
 // Rows of a tile are output rows in output order; each lane maps its row back to the patch
 // (item, tp, hp, wp) through the raster or merge-window order, so the order costs only index
 // arithmetic and the stores stay row-contiguous.
+#pragma once
+
 #include <type_traits>
 #include <utility>
 
@@ -980,33 +985,8 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
 // ----------------------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------------------
-hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, bool rows_map, hipStream_t st) {
-    const int S = packed_steps(P, w_esz);
-    const int64_t total = (int64_t)S * packed_cols(E, w_esz) * 4;
-    const int threads = 256;
-    const int blocks = (int)((total + threads - 1) / threads);
-    if (w_esz == 2)
-        hipLaunchKernelGGL(pe_pack_kernel<uint16_t>, dim3(blocks), dim3(threads), 0, st,
-                           static_cast<const uint16_t *>(w), static_cast<uint16_t *>(wpk), P, E, S, rows_map ? 1 : 0);
-    else
-        hipLaunchKernelGGL(pe_pack_kernel<float>, dim3(blocks), dim3(threads), 0, st,
-                           static_cast<const float *>(w), static_cast<float *>(wpk), P, E, S, 0);
-    return hipGetLastError();
-}
-
-hipError_t launch_bias(const void *b, int b_esz, float *bias32, int E, hipStream_t st) {
-    const int threads = 256, blocks = (E + threads - 1) / threads;
-    if (b_esz == 2)
-        hipLaunchKernelGGL(pe_bias_kernel<__bf16>, dim3(blocks), dim3(threads), 0, st,
-                           static_cast<const __bf16 *>(b), bias32, E);
-    else
-        hipLaunchKernelGGL(pe_bias_kernel<float>, dim3(blocks), dim3(threads), 0, st,
-                           static_cast<const float *>(b), bias32, E);
-    return hipGetLastError();
-}
-
 template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
-static hipError_t launch16(FwdArgs a, hipStream_t st) {
+inline hipError_t launch16(FwdArgs a, hipStream_t st) {
     constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
@@ -1016,7 +996,7 @@ static hipError_t launch16(FwdArgs a, hipStream_t st) {
 }
 
 template <int P, int ISZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD>
-static hipError_t launch32(FwdArgs a, hipStream_t st) {
+inline hipError_t launch32(FwdArgs a, hipStream_t st) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
@@ -1031,7 +1011,7 @@ static hipError_t launch32(FwdArgs a, hipStream_t st) {
 }
 
 template <int P, int ISZ, int OSZ, int TM, int TN, int AD>
-static hipError_t launch_sk(FwdArgs a, hipStream_t st) {
+inline hipError_t launch_sk(FwdArgs a, hipStream_t st) {
     constexpr int BM = TM * 32, BN = TN * 32;
     a.tiles_m = (a.n_rows + BM - 1) / BM;
     a.tiles_n = (a.E + BN - 1) / BN;
@@ -1066,7 +1046,7 @@ __host__ inline int choose_tiles(int64_t n_rows, int E, int num_cus) {
 // ESZ: weight element size; ISZ: input element size (fp32 input meets a bf16 weight by rounding
 // on load)
 template <int P, int ESZ, int ISZ, int OSZ>
-static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
+inline hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
     if constexpr (ESZ == 4) {
         // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps)
         return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
@@ -1082,20 +1062,6 @@ static hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
                 return launch_sk<P, ISZ, OSZ, 1, 4, 2>(a, st);
         }
     }
-}
-
-hipError_t launch_forward(const FwdArgs &a, int P, int w_esz, int in_esz, int out_esz, hipStream_t st) {
-    if (w_esz == 4) {  // fp32 weight: fp32 input
-        if (in_esz != 4) return hipErrorInvalidValue;
-        if (P == 14) return out_esz == 2 ? launch_p<14, 4, 4, 2>(a, st) : launch_p<14, 4, 4, 4>(a, st);
-        return out_esz == 2 ? launch_p<16, 4, 4, 2>(a, st) : launch_p<16, 4, 4, 4>(a, st);
-    }
-    if (P == 14) {
-        if (in_esz == 2) return out_esz == 2 ? launch_p<14, 2, 2, 2>(a, st) : launch_p<14, 2, 2, 4>(a, st);
-        return out_esz == 2 ? launch_p<14, 2, 4, 2>(a, st) : launch_p<14, 2, 4, 4>(a, st);
-    }
-    if (in_esz == 2) return out_esz == 2 ? launch_p<16, 2, 2, 2>(a, st) : launch_p<16, 2, 2, 4>(a, st);
-    return out_esz == 2 ? launch_p<16, 2, 4, 2>(a, st) : launch_p<16, 2, 4, 4>(a, st);
 }
 
 }  // namespace pe
