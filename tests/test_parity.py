@@ -140,6 +140,10 @@ CASES = [
     ("single_patch", 14, 1280, [(1, 1, 1, 1)], "raster", torch.bfloat16, torch.bfloat16, True),
     ("large_merge_2k", 14, 1280, [(1, 40, 52, 1)], "merge", torch.bfloat16, torch.bfloat16, True),
     ("tall_video_big_tiles", 14, 1280, [(8, 24, 24, 16)], "merge", torch.bfloat16, torch.bfloat16, False),
+    # one frame size, image-ness changing from item to item: a launch per run of images / videos
+    ("images_and_videos_one_size", 14, 640, [(1, 4, 6, 1), (2, 4, 6, 3), (1, 4, 6, 1), (1, 4, 6, 2),
+                                             (1, 4, 6, 1)], "merge", torch.bfloat16, torch.bfloat16, True),
+    ("t1_two_frames", 14, 320, [(1, 6, 4, 2)], "raster", torch.bfloat16, torch.bfloat16, False),
 ]
 
 
@@ -233,6 +237,23 @@ def test_fp32_input_bf16_weight(pe, case):
         got, ref, od = run(pe, case, x, w, b, grid, [F for (*_, F) in items], order="merge",
                            out_dtype=torch.bfloat16, rows=rows)
     check(got, ref, od, case)
+
+
+def test_images_and_videos_large(pe):
+    """Images and a video of one frame size at a size that uses the large-tile kernels: the
+    library splits the call into launches by image-ness; rows sampled."""
+    P, E = 14, 1280
+    K = 3 * 2 * P * P
+    items = [(1, 32, 32, 1)] * 3 + [(2, 32, 32, 4)] + [(1, 32, 32, 1)] * 3
+    xs = [make(900 + i, (F, 3, h * P, ww * P), torch.bfloat16) for i, (t, h, ww, F) in enumerate(items)]
+    x = torch.cat([a.reshape(-1) for a in xs])
+    w = make(901, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(902, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    grid = [[t, h, ww] for (t, h, ww, F) in items]
+    n = sum(t * h * ww for (t, h, ww) in grid)
+    got, ref, od = run(pe, "images_and_video_large", x, w, b, grid, [F for (*_, F) in items], order="merge",
+                       rows=sampled_rows(n, 23, 500))
+    check(got, ref, od, "images and video")
 
 
 def test_many_items_split_launches(pe):
