@@ -617,7 +617,22 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     constexpr int EP_PITCH = TN * 32 + 8;           // dwords
     constexpr int EP_WAVE = 16 * EP_PITCH * 4;      // bytes per wave
     constexpr int KBUF = KS * STAGE;
-    constexpr int LDS_BYTES = (2 * KBUF > EP_WAVE * WM * WN) ? 2 * KBUF : EP_WAVE * WM * WN;
+    // Patch rows stage A through LDS as well: each row's k-steps are 128-byte pieces of one
+    // contiguous row, loaded by consecutive threads (eight rows per load instruction, every
+    // cache line fetched whole) into two LDS stages of BM rows (pitch 144 bytes: the 16 lanes of
+    // a 16-byte read land on distinct banks), and read back as the matrix-core fragments.
+    constexpr bool AST = AM == kARows;
+    static_assert(!AST || KS == 1, "patch rows: one weight k-step per LDS buffer");
+    constexpr int AC = ISZ == 2 ? 2 : 1;           // k-steps per 128-byte A piece
+    constexpr int NCH = (S + AC - 1) / AC;         // A pieces per row
+    constexpr int APITCH = 144;
+    constexpr int ASTAGE = BM * APITCH;
+    constexpr int AL = BM * 8 / NT;                // 16-byte A loads per thread per piece
+    static_assert(!AST || (BM * 8) % NT == 0, "A piece loads");
+    constexpr int AOFF = 2 * KBUF;                 // A stages after the weight buffers
+    constexpr int MAIN_BYTES = 2 * KBUF + (AST ? 2 * ASTAGE : 0);
+    constexpr int LDS_BYTES = (MAIN_BYTES > EP_WAVE * WM * WN) ? MAIN_BYTES : EP_WAVE * WM * WN;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
     // ---- tile: blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous run of
@@ -660,6 +675,53 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         load_a_step<P, TM, AM, ISZ, decltype(sc)::value>(rsrc, vb, plane, rstr, h, dst);
     };
 
+    // Patch rows: thread piece loads. Load i of a piece: row (i*NT + tid) / 8 of the tile, its
+    // 16-byte part (i*NT + tid) % 8; rows past the end read row 0 of the launch (never stored).
+    constexpr int KB = kC * kTp * P * P * ISZ;     // bytes of one patch row
+    uint32_t av[AST ? AL : 1];
+    int apart[AST ? AL : 1];
+    if constexpr (AST) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            const int q = i * NT + tid, r = q >> 3;
+            apart[i] = q & 7;
+            const int row = row0 + r;
+            av[i] = (row < a.n_rows ? (uint32_t)row * (uint32_t)KB : 0u) + (uint32_t)apart[i] * 16u;
+        }
+    }
+    auto load_piece = [&](auto cc, u32x4 (&dst)[AST ? AL : 1]) {
+        constexpr int c = decltype(cc)::value;
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)av[i], c * 128, 0);
+            // bytes past the row (the last piece) belong to the next row: zero them
+            if constexpr (c * 128 + 128 > KB) {
+                if (c * 128 + apart[i] * 16 >= KB) dst[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto store_piece = [&](int c, const u32x4 (&src)[AST ? AL : 1]) {
+        unsigned char *st = lds + AOFF + (c & 1) * ASTAGE;
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            const int q = i * NT + tid;
+            *reinterpret_cast<u32x4 *>(st + (q >> 3) * APITCH + (q & 7) * 16) = src[i];
+        }
+    };
+    // fragments of k-step s for this lane from the A stage: row (wm*TM + rb)*32 + l32, elements
+    // 32*(s % AC)... of the piece: bytes (s % AC)*64 + (2j + h)*16*ISZ/2
+    auto read_a = [&](int s, AFrag<ISZ> (&dst)[TM][2]) {
+        const unsigned char *st = lds + AOFF + ((s / AC) & 1) * ASTAGE;
+#pragma unroll
+        for (int rb = 0; rb < TM; ++rb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const unsigned char *src = st + ((wm * TM + rb) * 32 + l32) * APITCH + (s % AC) * 64 + (2 * j + h) * 8 * ISZ;
+#pragma unroll
+                for (int d = 0; d < ISZ / 2; ++d) dst[rb][j].d[d] = *reinterpret_cast<const u32x4 *>(src + 16 * d);
+            }
+    };
+
     // Packed weight of k-step s for the tile's columns: BN*64 contiguous bytes. Chunks past the
     // last column block get an offset beyond the buffer range and read 0 (no branches: branches
     // would make the wait counts conservative).
@@ -698,8 +760,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         for (int rb = 0; rb < TM; ++rb) acc[rb][cb] = b16;
     }
 
-    auto compute = [&](auto sc, const AFrag<ISZ> (&ald)[TM][2]) {
+    auto compute = [&](auto sc, const AFrag<ISZ> (&ald_regs)[TM][2]) {
         constexpr int s = decltype(sc)::value;
+        AFrag<ISZ> ald_lds[TM][2];
+        if constexpr (AST) read_a(s, ald_lds);
+        const AFrag<ISZ>(&ald)[TM][2] = AST ? ald_lds : ald_regs;
         u32x4 af[TM][2];
         a_operands<P, TM, AM, ISZ, s>(ald, af);
         // fragment (j, cb) of this step: 1 KB at stage + (wn*TN + cb)*2 KB + j*1 KB
@@ -724,7 +789,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         }
         // Pin the interleave: PF fragment reads first, then per fragment its TM products and the
         // read PF fragments ahead (left alone, the scheduler sinks each read next to its use).
-        __builtin_amdgcn_sched_group_barrier(0x100, PF < NF ? PF : NF, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, (PF < NF ? PF : NF) + (AST ? TM * 2 * (ISZ / 2) : 0), 0);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
             __builtin_amdgcn_sched_group_barrier(0x008, TM, 0);
@@ -738,11 +803,22 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     // barrier per KS k-steps); while the waves compute from one buffer they fill the other one
     // k-step at a time from a BD-deep register ring (each weight k-step is loaded BD-1 k-steps
     // before it is stored).
-    constexpr bool PAIR = AM == kARows;
-    constexpr int RD = PAIR ? AD + 2 : AD + 1;           // A ring depth
-    constexpr int PRE = PAIR ? (AD + 1) / 2 * 2 : AD;    // A k-steps loaded before the loop
+    // Patch rows: A piece c (k-steps AC*c ..) is loaded at k-step AC*c - 3 and stored into stage
+    // c & 1 at the end of k-step AC*c - 1 (its barrier publishes it); at most three pieces are in
+    // registers at once.
+    constexpr int RD = AST ? 1 : AD + 1;                 // A ring depth (frames)
+    constexpr int PRE = AST ? 0 : AD;                    // A k-steps loaded before the loop (frames)
     AFrag<ISZ> Ar[RD][TM][2];
+    u32x4 Apc[AST ? 3 : 1][AST ? AL : 1];
     u32x4 Br[BD][CH];
+    if constexpr (AST) {
+        load_piece(IC<0>{}, Apc[0]);
+        store_piece(0, Apc[0]);
+        static_for<NCH>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            if constexpr (c >= 1 && AC * c - 3 < 0) load_piece(cc, Apc[c % 3]);
+        });
+    }
     {
         u32x4 tmp[CH];
 #pragma unroll
@@ -761,14 +837,19 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         constexpr int s = decltype(sc)::value;
         constexpr int t = s + KS;
         if constexpr (t + BD - 1 < S) load_b(t + BD - 1, Br[(t + BD - 1) % BD]);
-        if constexpr (!PAIR) {
-            if constexpr (s + AD < S) load_a(IC<s + AD>{}, Ar[(s + AD) % RD]);
-        } else if constexpr ((s + AD) % 2 == 0 && s + AD >= PRE) {
-            if constexpr (s + AD < S) load_a(IC<s + AD>{}, Ar[(s + AD) % RD]);
-            if constexpr (s + AD + 1 < S) load_a(IC<s + AD + 1>{}, Ar[(s + AD + 1) % RD]);
+        if constexpr (AST) {
+            // piece c with AC*c - 3 == s
+            if constexpr ((s + 3) % AC == 0 && (s + 3) / AC < NCH && (s + 3) / AC >= 1)
+                load_piece(IC<(s + 3) / AC>{}, Apc[((s + 3) / AC) % 3]);
+        } else if constexpr (s + AD < S) {
+            load_a(IC<s + AD>{}, Ar[(s + AD) % RD]);
         }
         compute(sc, Ar[s % RD]);
         if constexpr (t < S) store_b(t, Br[t % BD]);
+        if constexpr (AST) {
+            // piece c with AC*c - 1 == s
+            if constexpr ((s + 1) % AC == 0 && (s + 1) / AC < NCH) store_piece((s + 1) / AC, Apc[((s + 1) / AC) % 3]);
+        }
         if constexpr (s % KS == KS - 1 && s + 1 < S) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     });
