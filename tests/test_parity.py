@@ -256,6 +256,38 @@ def test_images_and_videos_large(pe):
     check(got, ref, od, "images and video")
 
 
+def test_concurrent_streams_one_handle(pe):
+    """The handle is immutable: calls on two streams at once (different inputs, sizes and so
+    kernels) give the same results as the oracle."""
+    P, E = 14, 1280
+    K = 3 * 2 * P * P
+    w = make(950, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(951, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV), order="merge")
+    x1 = make(952, (1, 3, 16 * P, 64 * P), torch.bfloat16)       # 1024 patches: split-k
+    x2 = make(953, (8, 3, 32 * P, 32 * P), torch.bfloat16)       # 8192 patches: large tiles
+    g1, g2 = [[1, 16, 64]], [[1, 32, 32]] * 8
+    say("two streams: %s and %s" % (g1, "8 x [1, 32, 32]"))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    d1, d2 = x1.to(DEV), x2.to(DEV)
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            o1 = mod(d1, g1, [1])
+        with torch.cuda.stream(s2):
+            o2 = mod(d2, g2, [1] * 8)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    r1 = oracle.forward(x1, w, b, grid=g1, frames=[1], order="merge")
+    rows2 = sampled_rows(8192, 29, 300)
+    r2 = oracle.forward(x2, w, b, grid=g2, frames=[1] * 8, order="merge", rows=rows2)
+    for o1, o2 in outs:
+        check(o1.float().cpu().double().numpy(), r1, torch.bfloat16, "stream 1")
+        check(o2[torch.as_tensor(rows2, device=DEV)].float().cpu().double().numpy(), r2, torch.bfloat16, "stream 2")
+    mod.close()
+
+
 def test_many_items_split_launches(pe):
     """More items than one launch's item table holds: the library splits the launches."""
     P, E = 14, 256
