@@ -70,9 +70,13 @@ def dominant_kernel(wl, num_cus=256):
     return "pe_fwd32_kernel" if min(c256, c128) <= csk else "pe_fwd32_sk_kernel"
 
 
-def time_workload(idx, steps, warmup, graph=True, rows=False):
+def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=10, cold=False):
     """rows: feed the workload's patches as pre-flattened rows [N, K] (the processor's
-    pixel_values layout) instead of its frames: same N, weight and bias, synthetic N(0, 1) rows."""
+    pixel_values layout) instead of its frames: same N, weight and bias, synthetic N(0, 1) rows.
+    items: keep only the first `items` items (one GPU's share of an item split).
+    The graph of K steps is replayed `reps` times, each replay timed: median, p10 and p90 per step.
+    cold: also time single launches after overwriting a 1 GiB buffer (L2 and the 256 MB
+    Infinity Cache hold nothing of the inputs), median of `reps`."""
     import torch
     import workloads
     import vlm_vision_patch_amd as pe
@@ -80,6 +84,9 @@ def time_workload(idx, steps, warmup, graph=True, rows=False):
     wl = workloads.WORKLOADS[idx]
     dev = torch.device("cuda:0")
     x, w, b = workloads.generate(wl)
+    if items is not None:
+        wl = workloads.share(wl, items)
+        x = x.reshape(-1)[:workloads.input_elements(wl)]
     n, flops, byts = algorithmic(wl, rows)
     kind = wl.kind
     grid, frames = [list(g) for g in wl.grid], list(wl.frames) or None
@@ -110,19 +117,73 @@ def time_workload(idx, steps, warmup, graph=True, rows=False):
         with torch.cuda.graph(g, stream=s):
             for _ in range(steps):
                 mod(x, grid, frames, kind=kind, out=out)
+        per = []
         with torch.cuda.stream(s):
             g.replay()                       # untimed: first replay uploads the graph
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(s)
-            g.replay()
-            e1.record(s)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / steps
-        timing = "K steps captured in one HIP graph, replayed once between HIP events"
+            for _ in range(max(1, reps)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                g.replay()
+                e1.record(s)
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) / steps)
+        per.sort()
+        ms = per[len(per) // 2]
+        stats = {"median_ms": round(ms, 6), "p10_ms": round(per[len(per) // 10], 6),
+                 "p90_ms": round(per[min(len(per) - 1, (9 * len(per)) // 10)], 6), "replays": len(per)}
+        timing = "K steps captured in one HIP graph; median over %d replays, each between HIP events" % len(per)
         del g
+    else:
+        stats = None
+    cold_ms = None
+    if cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        cs = []
+        with torch.cuda.stream(s):
+            for i in range(max(1, reps)):
+                flush.fill_(float(i))
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                mod(x, grid, frames, kind=kind, out=out)
+                e1.record(s)
+                torch.cuda.synchronize()
+                cs.append(e0.elapsed_time(e1))
+        cs.sort()
+        cold_ms = cs[len(cs) // 2]
+        del flush
     mod.close()
-    return dict(wl=wl, n=n, flops=flops, bytes=byts, ms=ms, eager_ms=eager_ms, timing=timing, rows=rows)
+    return dict(wl=wl, n=n, flops=flops, bytes=byts, ms=ms, eager_ms=eager_ms, timing=timing, rows=rows,
+                stats=stats, cold_ms=cold_ms)
+
+
+def time_linear_context(idx, steps=20):
+    """hipBLASLt (torch.nn.functional.linear) on the same product with the patches already
+    flattened into a contiguous [N, K] matrix: context for the gather-fused kernel, not a target."""
+    import torch
+    import workloads
+    wl = workloads.WORKLOADS[idx]
+    dev = torch.device("cuda:0")
+    _, w, b = workloads.generate(wl)
+    n = sum(t * h * ww for (t, h, ww) in wl.grid)
+    dt = workloads.DTYPES[wl.w_dtype]
+    a = workloads.random_tensor((n, wl.k), seed=2000 + idx, dtype=dt).to(dev)
+    w2 = w.reshape(wl.embed, wl.k).to(dev)
+    b2 = b.to(dev) if b is not None else None
+    for _ in range(3):
+        y = torch.nn.functional.linear(a, w2, b2)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        y = torch.nn.functional.linear(a, w2, b2)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del y, a
+    return {"what": "torch.nn.functional.linear (hipBLASLt) on a contiguous [N, K] patch matrix, same "
+                    "N, K, E, dtype and bias; the patchify gather not included", "ms_per_step": round(ms, 5),
+            "tflops": round(2.0 * n * wl.k * wl.embed / (ms / 1e3) / 1e12, 2), "steps": steps}
 
 
 def cpu_baseline(idx, min_seconds=10.0):
@@ -170,15 +231,23 @@ def load_traffic(kernel, workload):
     return None
 
 
+def workloads_name(idx):
+    import workloads
+    return workloads.WORKLOADS[idx].name
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--extra", type=str, default="5,5r,4,1",
+    ap.add_argument("--extra", type=str, default="5,5r,5s8,4,6,1",
                     help="comma-separated further workloads reported under 'also' ('' for none); "
-                         "a trailing r feeds that workload's patches as pre-flattened rows")
+                         "a trailing r feeds that workload's patches as pre-flattened rows; sN keeps "
+                         "its first N items (one GPU's share of an N-way item split)")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the library-GEMM context line (hipBLASLt on the same product)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time K launches from Python instead of a captured graph (for counter runs)")
@@ -205,7 +274,7 @@ def main():
         print(json.dumps({"copy_bytes": n * 4}), flush=True)
         return
 
-    r = time_workload(args.workload, args.steps, args.warmup, graph=not args.eager)
+    r = time_workload(args.workload, args.steps, args.warmup, graph=not args.eager, cold=not args.eager)
     wl = r["wl"]
     t_s = r["ms"] / 1e3
     tflops = r["flops"] / t_s / 1e12
@@ -228,11 +297,13 @@ def main():
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     also = {}
     for spec in [v.strip() for v in args.extra.split(",") if v.strip()]:
-        e, as_rows = int(spec.rstrip("r")), spec.endswith("r")
-        if e == args.workload and not as_rows:
+        as_rows = spec.endswith("r")
+        share = int(spec.split("s")[1]) if "s" in spec else None
+        e = int(spec.rstrip("r").split("s")[0])
+        if e == args.workload and not as_rows and share is None:
             continue
         st = max(5, min(args.steps, 50))
-        q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows)
+        q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows, items=share, reps=3)
         qt = q["ms"] / 1e3
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
         also[q["wl"].name + ("_as_patch_rows" if as_rows else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
@@ -240,6 +311,8 @@ def main():
                               "frac_matrix_peak": round(q["flops"] / qt / 1e12 / qpk, 4),
                               "frac_hbm": round(q["bytes"] / qt / 1e9 / PEAK_HBM_GBS, 4),
                               "n_patches": q["n"], "steps": st}
+    if not args.no_context and not args.eager:
+        also["context_library_gemm_" + workloads_name(5)] = time_linear_context(5)
     cpu = None if args.no_cpu else cpu_baseline(args.workload)
     line = {
         "metric": METRIC, "value": round(r["n"] / t_s, 1), "unit": "patches/s", "n_gpus": 1,
@@ -253,7 +326,8 @@ def main():
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 3), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "eager_ms_per_step": round(r["eager_ms"], 6),
-        "timing": r["timing"],
+        "timing": r["timing"], "timing_stats": r["stats"],
+        "cold_ms_per_step": round(r["cold_ms"], 6) if r["cold_ms"] is not None else None,
         "roofline": roof, "cpu_baseline": cpu, "also": also,
     }
     print(json.dumps(line), flush=True)

@@ -103,6 +103,22 @@ def test_workload_5_sampled(pe):
     print("%s: %d sampled rows, max err %.3g" % (wl.name, len(rows), e), flush=True)
 
 
+def test_workload_6_sampled(pe):
+    """The Qwen3-VL-2B-shaped workload (P16, E1024, bias) over items of mixed sizes: every item's
+    first and last rows plus a seeded sample."""
+    wl = workloads.WORKLOADS[6]
+    x, w, b = workloads.generate(wl)
+    n = sum(t * h * ww for (t, h, ww) in wl.grid)
+    starts = np.cumsum([0] + [t * h * ww for (t, h, ww) in wl.grid])
+    edges = set()
+    for s0, s1 in zip(starts[:-1], starts[1:]):
+        edges.update((int(s0), int(s0) + 1, int(s1) - 2, int(s1) - 1))
+    rows = np.array(sorted(edges | set(sampled_rows(n, 31, 700).tolist())), dtype=np.int64)
+    got, ref, od = run(pe, wl.name, x, w, b, [list(g) for g in wl.grid], list(wl.frames), order=wl.order,
+                       rows=rows)
+    check(got, ref, od, wl.name)
+
+
 def test_workload_5_raster_sampled(pe):
     """The same batch in raster order: the order is a free choice of the caller."""
     wl = workloads.WORKLOADS[5]
@@ -286,6 +302,34 @@ def test_concurrent_streams_one_handle(pe):
         check(o1.float().cpu().double().numpy(), r1, torch.bfloat16, "stream 1")
         check(o2[torch.as_tensor(rows2, device=DEV)].float().cpu().double().numpy(), r2, torch.bfloat16, "stream 2")
     mod.close()
+
+
+MIXED = {
+    # name: (items [(t, h, w, F)], dtype, order); frame sizes differ within one launch
+    "images_large": ([(1, 72, 72, 1), (1, 32, 48, 1), (1, 16, 64, 1), (1, 56, 40, 1), (1, 24, 24, 1),
+                      (1, 64, 64, 1), (1, 40, 30, 1), (1, 8, 8, 1)], torch.bfloat16, "merge"),
+    "videos": ([(2, 8, 6, 4), (1, 12, 10, 2), (3, 4, 4, 5)], torch.bfloat16, "merge"),
+    "images_f32_input": ([(1, 20, 30, 1), (1, 34, 18, 1), (1, 6, 4, 1)], torch.float32, "merge"),
+    "images_raster": ([(1, 9, 13, 1), (1, 40, 33, 1), (1, 1, 1, 1), (1, 25, 7, 1)], torch.bfloat16, "raster"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MIXED))
+def test_mixed_frame_sizes(pe, case):
+    """Items of different frame sizes in one launch: each lane uses its own item's strides."""
+    items, dt, order = MIXED[case]
+    P, E = 14, 1280
+    K = 3 * 2 * P * P
+    xs = [make(1000 + i, (F, 3, h * P, ww * P), dt) for i, (t, h, ww, F) in enumerate(items)]
+    x = torch.cat([a_.reshape(-1) for a_ in xs])
+    w = make(1001, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(1002, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    grid = [[t, h, ww] for (t, h, ww, F) in items]
+    n = sum(t * h * ww for (t, h, ww) in grid)
+    rows = None if n <= 3000 else sampled_rows(n, 37, 600)
+    got, ref, od = run(pe, "mixed_" + case, x, w, b, grid, [F for (*_, F) in items], order=order,
+                       out_dtype=torch.bfloat16, rows=rows)
+    check(got, ref, od, "mixed " + case)
 
 
 def test_many_items_split_launches(pe):

@@ -257,24 +257,26 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         return PE_OK;
     }
 
-    // frames: launches of at most kMaxItems consecutive items of one frame geometry (h, w), all
-    // single images or all not (the kernels load an image's shared temporal slots once), and at
-    // most kMaxLaunchBytes of input
+    // frames: launches of at most kMaxItems consecutive items, all single images or all not (the
+    // kernels load an image's shared temporal slots once), and at most kMaxLaunchBytes of input.
+    // Items of different frame sizes share a launch (the kernels then take each item's strides
+    // per lane instead of one scalar stride per launch).
     int64_t x0 = 0;  // element offset of item i0
     int i0 = 0;
     while (i0 < n_items) {
         int i1 = i0;
         int64_t span = 0;
-        while (i1 < n_items && i1 - i0 < pe::kMaxItems &&
-               grid_thw[3 * i1 + 1] == grid_thw[3 * i0 + 1] && grid_thw[3 * i1 + 2] == grid_thw[3 * i0 + 2] &&
-               (F[i1] == 1) == (F[i0] == 1) &&
+        bool mixed = false;
+        while (i1 < n_items && i1 - i0 < pe::kMaxItems && (F[i1] == 1) == (F[i0] == 1) &&
                (uint64_t)(span + elems[i1]) * ies <= kMaxLaunchBytes) {
             span += elems[i1];
+            mixed = mixed || grid_thw[3 * i1 + 1] != grid_thw[3 * i0 + 1] || grid_thw[3 * i1 + 2] != grid_thw[3 * i0 + 2];
             ++i1;
         }
         a.kind = 1;
         a.wpk = h->wpk;
         a.img = F[i0] == 1 ? 1 : 0;
+        a.mixg = mixed ? 1 : 0;
         a.rstr = (uint32_t)grid_thw[3 * i0 + 2] * (uint32_t)P;
         a.plane = (uint32_t)grid_thw[3 * i0 + 1] * (uint32_t)P * a.rstr;
         a.in = static_cast<const char *>(input) + x0 * ies;

@@ -36,8 +36,9 @@ struct FwdArgs {
     int32_t tiles_m, tiles_n;
     int32_t colmajor;      // tile order within an XCD's run: 1 = column tiles outermost
     int32_t img;           // 1: frames launch whose items are all single images (F = 1)
+    int32_t mixg;          // 1: frames launch whose items differ in frame size (h, w)
     int32_t num_cus;       // compute units of the device (tile-size choice)
-    uint32_t plane, rstr;  // channel and pixel-row strides (elements), the same for every row
+    uint32_t plane, rstr;  // channel and pixel-row strides (elements) when every item has one frame size
     Item items[kMaxItems];
 };
 

@@ -288,10 +288,18 @@ __device__ constexpr bool img_paired() {
 }
 // Issue the A loads of k-step s for TM 32-row blocks (vb: per-lane byte offset of the lane's
 // patch and temporal slot, or of its patch row plus 8 elements for lanes 32-63). Paired image
-// steps leave their two fragments in dst[rb][0].
-template <int P, int TM, int AM, int ISZ, int s>
+// steps leave their two fragments in dst[rb][0]. With one frame geometry per launch (MG false) the
+// per-step part of every address is one scalar for the whole launch; with items of different
+// frame sizes in one launch (MG true) each lane adds its own item's channel plane and pixel-row
+// stride (vpl, vrs) instead: two multiply-adds per fragment.
+template <int P, int TM, int AM, int ISZ, int s, bool MG = false>
 __device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&vb)[TM],
-                                            uint32_t plane, uint32_t rstr, int h, AFrag<ISZ> (&dst)[TM][2]) {
+                                            uint32_t plane, uint32_t rstr, int h, AFrag<ISZ> (&dst)[TM][2],
+                                            const uint32_t (&vpl)[TM], const uint32_t (&vrs)[TM]) {
+    // byte offset of (u, x) for block rb: uniform scalar, or per lane
+    auto off = [&](int rb, int u, int x) -> uint32_t {
+        return MG ? frag_off<P, ISZ>(u, x, vpl[rb], vrs[rb]) : frag_off<P, ISZ>(u, x, plane, rstr);
+    };
     if constexpr (AM == kARows) {
         constexpr int K = kC * kTp * P * P;
         static_for<2>([&](auto jc) {
@@ -313,32 +321,48 @@ __device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const u
         });
     } else if constexpr (AM == kAImage && img_paired<P, s>()) {
         constexpr UFrag f0 = tt_frag(P, 2 * s), f1 = tt_frag(P, 2 * s + 1);
-        const uint32_t o0 = frag_off<P, ISZ>(f0.u1, f0.x1, plane, rstr);
-        const uint32_t hd = h ? frag_off<P, ISZ>(f1.u1, f1.x1, plane, rstr) - o0 : 0u;
-        if constexpr (f0.kind == kUfFull) {
+        if constexpr (!MG) {
+            const uint32_t o0 = off(0, f0.u1, f0.x1);
+            const uint32_t hd = h ? off(0, f1.u1, f1.x1) - o0 : 0u;
+            if constexpr (f0.kind == kUfFull) {
 #pragma unroll
-            for (int rb = 0; rb < TM; ++rb) ld_whole<ISZ>(rsrc, vb[rb] + hd, (int)o0, dst[rb][0]);
+                for (int rb = 0; rb < TM; ++rb) ld_whole<ISZ>(rsrc, vb[rb] + hd, (int)o0, dst[rb][0]);
+            } else {
+                const uint32_t p0 = off(0, f0.u2, f0.x2);
+                const uint32_t hd2 = h ? off(0, f1.u2, f1.x2) - p0 : 0u;
+#pragma unroll
+                for (int rb = 0; rb < TM; ++rb)
+                    ld_split62<ISZ>(rsrc, vb[rb] + hd, (int)o0, vb[rb] + hd2, (int)p0, dst[rb][0]);
+            }
         } else {
-            const uint32_t p0 = frag_off<P, ISZ>(f0.u2, f0.x2, plane, rstr);
-            const uint32_t hd2 = h ? frag_off<P, ISZ>(f1.u2, f1.x2, plane, rstr) - p0 : 0u;
 #pragma unroll
-            for (int rb = 0; rb < TM; ++rb)
-                ld_split62<ISZ>(rsrc, vb[rb] + hd, (int)o0, vb[rb] + hd2, (int)p0, dst[rb][0]);
+            for (int rb = 0; rb < TM; ++rb) {
+                const uint32_t v1 = vb[rb] + (h ? off(rb, f1.u1, f1.x1) : off(rb, f0.u1, f0.x1));
+                if constexpr (f0.kind == kUfFull) {
+                    ld_whole<ISZ>(rsrc, v1, 0, dst[rb][0]);
+                } else {
+                    const uint32_t v2 = vb[rb] + (h ? off(rb, f1.u2, f1.x2) : off(rb, f0.u2, f0.x2));
+                    ld_split62<ISZ>(rsrc, v1, 0, v2, 0, dst[rb][0]);
+                }
+            }
         }
     } else {
         static_for<2>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             constexpr UFrag f = tt_frag(P, 2 * s + j);
-            const int so1 = (int)frag_off<P, ISZ>(f.u1, f.x1, plane, rstr);
 #pragma unroll
             for (int rb = 0; rb < TM; ++rb) {
+                // (vector, scalar) offsets of the two pieces
+                const uint32_t v1 = MG ? vb[rb] + off(rb, f.u1, f.x1) : vb[rb];
+                const int so1 = MG ? 0 : (int)off(0, f.u1, f.x1);
                 if constexpr (f.kind == kUfFull) {
-                    ld_whole<ISZ>(rsrc, vb[rb], so1, dst[rb][j]);
+                    ld_whole<ISZ>(rsrc, v1, so1, dst[rb][j]);
                 } else if constexpr (f.kind == kUfSplit62) {
-                    const int so2 = (int)frag_off<P, ISZ>(f.u2, f.x2, plane, rstr);
-                    ld_split62<ISZ>(rsrc, vb[rb], so1, vb[rb], so2, dst[rb][j]);
+                    const uint32_t v2 = MG ? vb[rb] + off(rb, f.u2, f.x2) : vb[rb];
+                    const int so2 = MG ? 0 : (int)off(0, f.u2, f.x2);
+                    ld_split62<ISZ>(rsrc, v1, so1, v2, so2, dst[rb][j]);
                 } else {
-                    ld_tail4<ISZ>(rsrc, vb[rb], so1, dst[rb][j]);
+                    ld_tail4<ISZ>(rsrc, v1, so1, dst[rb][j]);
                 }
             }
         });
@@ -602,7 +626,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs 
 // ----------------------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int P, int ISZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD, int AM>
+template <int P, int ISZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD, int AM, bool MG>
 __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs a) {
     constexpr int ESZ = 2;
     constexpr int NT = WM * WN * 64;
@@ -658,11 +682,13 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     // patch rows the row plus 8 elements for lanes 32-63. The per-step part of each address is the
     // same for every row of the launch (one frame geometry per launch), so it is a scalar offset
     // and the loads cost no vector arithmetic.
-    uint32_t vb[TM];
+    uint32_t vb[TM], vpl[TM], vrs[TM];
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
         const PatchRef p = patch_of_row<P>(a, row0 + (wm * TM + rb) * 32 + l32);
         vb[rb] = AM == kARows ? (p.base + (h ? 8u : 0u)) * (uint32_t)ISZ : (p.base + (h ? p.tstr : 0u)) * (uint32_t)ISZ;
+        vpl[rb] = p.plane;
+        vrs[rb] = p.rstr;
     }
 
     const __amdgpu_buffer_rsrc_t rsrc =
@@ -672,7 +698,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     // A fragments of k-step s (sub-steps j = 0, 1). Loads only; the data is first used by the
     // step's matrix products.
     auto load_a = [&](auto sc, AFrag<ISZ> (&dst)[TM][2]) {
-        load_a_step<P, TM, AM, ISZ, decltype(sc)::value>(rsrc, vb, plane, rstr, h, dst);
+        load_a_step<P, TM, AM, ISZ, decltype(sc)::value, MG>(rsrc, vb, plane, rstr, h, dst, vpl, vrs);
     };
 
     // Patch rows: thread piece loads. Load i of a piece: row (i*NT + tid) / 8 of the tile, its
@@ -914,7 +940,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 // go from global memory straight to registers, with no LDS stage and no barrier in the k loop.
 // The four fp32 partial tiles meet in LDS at the end and are summed in a fixed order.
 // ----------------------------------------------------------------------------------------
-template <int P, int ISZ, int OSZ, int TM, int TN, int AD, int AM>
+template <int P, int ISZ, int OSZ, int TM, int TN, int AD, int AM, bool MG>
 __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     constexpr int NW = 4;
     constexpr int BM = TM * 32, BN = TN * 32;
@@ -939,11 +965,13 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     const int h = lane >> 5, l32 = lane & 31;
     const int ncb = packed_cols(a.E, 2) >> 5;
 
-    uint32_t vb[TM];
+    uint32_t vb[TM], vpl[TM], vrs[TM];
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
         const PatchRef p = patch_of_row<P>(a, row0 + rb * 32 + l32);
         vb[rb] = AM == kARows ? (p.base + (h ? 8u : 0u)) * (uint32_t)ISZ : (p.base + (h ? p.tstr : 0u)) * (uint32_t)ISZ;
+        vpl[rb] = p.plane;
+        vrs[rb] = p.rstr;
     }
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.in), (short)0, (int)a.in_bytes, kBufWord3);
@@ -971,7 +999,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     struct Frags { AFrag<ISZ> a[TM][2]; u32x4 b[TN][2]; };
     auto load = [&](auto sc, Frags &d) {
         constexpr int s = decltype(sc)::value;
-        load_a_step<P, TM, AM, ISZ, s>(rsrc, vb, plane, rstr, h, d.a);
+        load_a_step<P, TM, AM, ISZ, s, MG>(rsrc, vb, plane, rstr, h, d.a, vpl, vrs);
         static_for<2>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             const int sw = (int)(((uint32_t)s * (uint32_t)ncb * 2u + j) * 1024u);
@@ -1083,11 +1111,15 @@ inline hipError_t launch32(FwdArgs a, hipStream_t st) {
     a.tiles_n = (a.E + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
     if (a.kind == 0)
-        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kARows>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kARows, false>), grid, block, 0, st, a);
+    else if (a.img && a.mixg)
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAImage, true>), grid, block, 0, st, a);
     else if (a.img)
-        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAImage>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAImage, false>), grid, block, 0, st, a);
+    else if (a.mixg)
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAFrames, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAFrames>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAFrames, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -1098,11 +1130,15 @@ inline hipError_t launch_sk(FwdArgs a, hipStream_t st) {
     a.tiles_n = (a.E + BN - 1) / BN;
     const dim3 grid(a.tiles_m * a.tiles_n), block(256);
     if (a.kind == 0)
-        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kARows>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kARows, false>), grid, block, 0, st, a);
+    else if (a.img && a.mixg)
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAImage, true>), grid, block, 0, st, a);
     else if (a.img)
-        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAImage>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAImage, false>), grid, block, 0, st, a);
+    else if (a.mixg)
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAFrames, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAFrames>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAFrames, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 

@@ -74,7 +74,34 @@ WORKLOADS = {
                 "merge", tuple((1, 72, 72) for _ in range(64)), tuple(1 for _ in range(64)),
                 (64, 3, 1008, 1008),
                 note="64 images, each frame duplicated; throughput batch"),
+    # Qwen3-VL-2B-shaped vision PatchEmbed ("Optimize VLM PatchEmbed": patch 16, hidden 1024,
+    # Conv3d with bias) over a batch of items of different sizes: images and one video.
+    6: Workload(6, "qwen3vl2b_p16_e1024_mixed", "frames", "bf16", "bf16", "bf16", 16, 1024, True,
+                "merge", ((1, 32, 32), (1, 48, 64), (2, 32, 32), (1, 24, 40), (1, 32, 32)),
+                (1, 1, 4, 1, 1),
+                (3 * 16 * 16 * (32 * 32 + 48 * 64 + 4 * 32 * 32 + 24 * 40 + 32 * 32),),
+                note="mixed sizes: four images and a 4-frame video, items back to back"),
 }
+
+
+def input_elements(wl: Workload) -> int:
+    """Elements of the whole input buffer."""
+    n = 1
+    for d in wl.input_shape:
+        n *= d
+    return n
+
+
+def share(wl: Workload, items: int) -> Workload:
+    """The first `items` items of a frames workload (one GPU's share of an item split); its
+    input is the leading part of the whole input buffer."""
+    if wl.kind != "frames":
+        raise ValueError("item shares apply to frames workloads")
+    grid, frames = wl.grid[:items], wl.frames[:items]
+    elems = sum(f * wl.channels * (h * wl.patch) * (w * wl.patch) for (t, h, w), f in zip(grid, frames))
+    return Workload(wl.index, "%s_share%d" % (wl.name, items), wl.kind, wl.in_dtype, wl.w_dtype,
+                    wl.out_dtype, wl.patch, wl.embed, wl.bias, wl.order, grid, frames, (elems,),
+                    wl.channels, wl.temporal, wl.merge, "first %d items of %s" % (items, wl.name))
 
 
 def generate(wl: Workload, seed: int | None = None):
