@@ -35,7 +35,7 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(wl, rows=False):
+def algorithmic(wl, rows=False, add=False):
     """FLOPs and algorithmic HBM bytes of one step: unique input read once (one frame per image,
     every frame of a video; patch rows as given), packed weight, bias, output. rows: the same
     patches given as pre-flattened rows [N, K]."""
@@ -47,7 +47,7 @@ def algorithmic(wl, rows=False):
     for d in (wl.input_shape if not rows else (n, wl.k)):
         inp *= d
     byts = inp * esz[wl.in_dtype] + wl.embed * wl.k * esz[wl.w_dtype] + \
-        (wl.embed * esz[wl.w_dtype] if wl.bias else 0) + n * wl.embed * esz[wl.out_dtype]
+        (wl.embed * esz[wl.w_dtype] if wl.bias else 0) + n * wl.embed * esz[wl.out_dtype] * (2 if add else 1)
     return n, flops, byts
 
 
@@ -70,13 +70,14 @@ def dominant_kernel(wl, num_cus=256):
     return "pe_fwd32_kernel" if min(c256, c128) <= csk else "pe_fwd32_sk_kernel"
 
 
-def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=10, cold=False):
+def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=10, cold=False, add=False):
     """rows: feed the workload's patches as pre-flattened rows [N, K] (the processor's
     pixel_values layout) instead of its frames: same N, weight and bias, synthetic N(0, 1) rows.
     items: keep only the first `items` items (one GPU's share of an item split).
     The graph of K steps is replayed `reps` times, each replay timed: median, p10 and p90 per step.
     cold: also time single launches after overwriting a 1 GiB buffer (L2 and the 256 MB
-    Infinity Cache hold nothing of the inputs), median of `reps`."""
+    Infinity Cache hold nothing of the inputs), median of `reps`.
+    add: fuse the add of a synthetic [N, E] tensor (position embeddings) into the epilogue."""
     import torch
     import workloads
     import vlm_vision_patch_amd as pe
@@ -87,7 +88,7 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     if items is not None:
         wl = workloads.share(wl, items)
         x = x.reshape(-1)[:workloads.input_elements(wl)]
-    n, flops, byts = algorithmic(wl, rows)
+    n, flops, byts = algorithmic(wl, rows, add)
     kind = wl.kind
     grid, frames = [list(g) for g in wl.grid], list(wl.frames) or None
     if rows:
@@ -97,16 +98,20 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     b = b.to(dev) if b is not None else None
     mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype])
     out = torch.empty((n, wl.embed), dtype=workloads.DTYPES[wl.out_dtype], device=dev)
+    addend = None
+    if add:
+        addend = (workloads.random_tensor((n, wl.embed), seed=3000 + idx) * 0.02).to(
+            workloads.DTYPES[wl.out_dtype]).to(dev)
     s = torch.cuda.Stream(device=dev)   # default priority
     with torch.cuda.stream(s):
         for _ in range(warmup):
-            mod(x, grid, frames, kind=kind, out=out)
+            mod(x, grid, frames, kind=kind, out=out, add=addend)
         # eager: K launches from Python
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(s)
         for _ in range(steps):
-            mod(x, grid, frames, kind=kind, out=out)
+            mod(x, grid, frames, kind=kind, out=out, add=addend)
         e1.record(s)
         torch.cuda.synchronize()
         eager_ms = e0.elapsed_time(e1) / steps
@@ -116,7 +121,7 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             for _ in range(steps):
-                mod(x, grid, frames, kind=kind, out=out)
+                mod(x, grid, frames, kind=kind, out=out, add=addend)
         per = []
         with torch.cuda.stream(s):
             g.replay()                       # untimed: first replay uploads the graph
@@ -145,7 +150,7 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
                 flush.fill_(float(i))
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(s)
-                mod(x, grid, frames, kind=kind, out=out)
+                mod(x, grid, frames, kind=kind, out=out, add=addend)
                 e1.record(s)
                 torch.cuda.synchronize()
                 cs.append(e0.elapsed_time(e1))
@@ -242,10 +247,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--extra", type=str, default="5,5r,5s8,4,6,1",
+    ap.add_argument("--extra", type=str, default="5,5r,5a,5s8,4,6,1",
                     help="comma-separated further workloads reported under 'also' ('' for none); "
-                         "a trailing r feeds that workload's patches as pre-flattened rows; sN keeps "
-                         "its first N items (one GPU's share of an N-way item split)")
+                         "a trailing r feeds that workload's patches as pre-flattened rows, a trailing "
+                         "a fuses the add of an [N, E] tensor; sN keeps its first N items (one GPU's "
+                         "share of an N-way item split)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the library-GEMM context line (hipBLASLt on the same product)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -298,15 +304,16 @@ def main():
     also = {}
     for spec in [v.strip() for v in args.extra.split(",") if v.strip()]:
         as_rows = spec.endswith("r")
+        with_add = spec.endswith("a")
         share = int(spec.split("s")[1]) if "s" in spec else None
-        e = int(spec.rstrip("r").split("s")[0])
+        e = int(spec.rstrip("ra").split("s")[0])
         if e == args.workload and not as_rows and share is None:
             continue
         st = max(5, min(args.steps, 50))
-        q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows, items=share, reps=3)
+        q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows, items=share, reps=3, add=with_add)
         qt = q["ms"] / 1e3
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
-        also[q["wl"].name + ("_as_patch_rows" if as_rows else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
+        also[q["wl"].name + ("_as_patch_rows" if as_rows else "") + ("_plus_pos_embed" if with_add else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
                               "tflops": round(q["flops"] / qt / 1e12, 2),
                               "frac_matrix_peak": round(q["flops"] / qt / 1e12 / qpk, 4),
                               "frac_hbm": round(q["bytes"] / qt / 1e9 / PEAK_HBM_GBS, 4),

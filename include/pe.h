@@ -117,6 +117,23 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
                const int32_t *grid_thw, const int32_t *frames, int32_t n_items, void *out,
                void *hip_stream);
 
+/*
+ * pe_forward_add -- out[N, E] = PatchEmbed(input) + addend, asynchronously on hip_stream.
+ *   The next step after the PatchEmbed in the Qwen3-VL vision forward adds the interpolated
+ *   position embeddings to its output ("Optimize VLM PatchEmbed", the Model forward:
+ *   hidden_states + pos_embeds). This call fuses that add into the PatchEmbed epilogue, saving a
+ *   separate pass over [N, E].
+ *   addend     device [N, E] row-major in the handle's out dtype, rows in the output order (the
+ *              order pe_forward writes); read only. May be the same buffer as out.
+ *   All other arguments as pe_forward.
+ * Arithmetic: the addend value is added in fp32 to the fp32 sum (products and bias), then one
+ * round-to-nearest-even cast to the output dtype (the module rounds twice: after the convolution
+ * and after the add). Returns as pe_forward, and PE_ERR_INVALID_ARG for a NULL addend.
+ */
+int pe_forward_add(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
+                   const int32_t *grid_thw, const int32_t *frames, int32_t n_items, const void *addend,
+                   void *out, void *hip_stream);
+
 /* N = sum over items of t*h*w ("freechatgpt/mytransformer" section 3.2: N = t*h*w), or a
  * negative pe_status for a NULL grid, negative n_items or a non-positive entry. */
 int64_t pe_num_rows(const int32_t *grid_thw, int32_t n_items);

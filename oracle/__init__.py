@@ -111,7 +111,7 @@ def row_positions(grid, frames=None, order="raster", m=2, C=3, Tp=2, P=14):
 
 
 def forward(x, w, b=None, *, grid, frames=None, kind="frames", order="raster", m=2,
-            rows=None, threads=None, cast_input_to=None):
+            rows=None, threads=None, cast_input_to=None, addend=None):
     """PatchEmbed in fp64. Returns a numpy array [n_rows, E] (all N rows if ``rows`` is None).
 
     x       frames kind: all items' frames back to back (any shape, flattened in C order);
@@ -121,6 +121,9 @@ def forward(x, w, b=None, *, grid, frames=None, kind="frames", order="raster", m
     grid    per item (t, h, w); frames: per item frame count (frames kind)
     cast_input_to  "bf16"/"f32": round the input to this dtype first (input cast to the
             weight dtype); None leaves the values as they are.
+    addend  [N, E] or None: added to the result row by row, in output row order (the Qwen3-VL
+            vision forward adds the interpolated position embeddings right after the PatchEmbed:
+            "Optimize VLM PatchEmbed", the Model forward, hidden_states + pos_embeds).
     """
     wd = _f64(w)
     if wd.ndim != 5:
@@ -149,4 +152,7 @@ def forward(x, w, b=None, *, grid, frames=None, kind="frames", order="raster", m
         _ptr(rr, ctypes.c_int64), n_out, _ptr(out, ctypes.c_double), int(threads))
     if rc != 0:
         raise ValueError("oracle forward failed (code %d)" % rc)
+    if addend is not None:
+        ad = _f64(addend).reshape(-1, E)
+        out += ad[rr] if rr is not None else ad
     return out

@@ -218,6 +218,28 @@ def test_linearity_and_bias_shift():
         np.max(np.abs(oracle.forward(x, W, b, **kw) - fx - b.numpy())) < 1e-13
 
 
+def test_addend_follows_output_rows():
+    """The fused add ("Optimize VLM PatchEmbed", the Model forward: hidden_states + pos_embeds):
+    with bias 0, adding the output for x2 to the output for x1 must give the output for x1 + x2
+    (linearity), in merge order over items of different sizes, so an addend taken in any other row
+    order fails; and a sampled-rows call takes the addend's rows at those positions."""
+    g = torch.Generator().manual_seed(14)
+    P, E = 2, 6
+    grid, frames = [[1, 4, 6], [2, 2, 4]], [1, 4]
+    n_x = 1 * 3 * 8 * 12 + 4 * 3 * 4 * 8
+    x1 = torch.randn(n_x, generator=g, dtype=torch.float64)
+    x2 = torch.randn(n_x, generator=g, dtype=torch.float64)
+    w = torch.randn(E, 3, 2, P, P, generator=g, dtype=torch.float64)
+    kw = dict(grid=grid, frames=frames, order="merge")
+    a2 = oracle.forward(x2, w, **kw)
+    got = oracle.forward(x1, w, addend=a2, **kw)
+    want = oracle.forward(x1 + x2, w, **kw)
+    assert np.abs(got - want).max() <= 1e-12 * max(1.0, np.abs(want).max())
+    rows = [0, 5, 17, 23, 24, 39]
+    sub = oracle.forward(x1, w, addend=a2, rows=rows, **kw)
+    assert np.array_equal(sub, got[rows])
+
+
 def test_duplicated_frame_equals_temporal_weight_sum():
     """A single image frame feeds both temporal slices, so the Conv3d equals a 2-D patch
     product with W[:, :, 0] + W[:, :, 1] (exact in fp64 for bf16 weights)."""

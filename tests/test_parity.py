@@ -47,13 +47,17 @@ def check(got, ref, out_dtype, what):
 
 
 def run(pe, name, x, w, b, grid, frames=None, kind="frames", order="raster", out_dtype=None,
-        rows=None):
+        rows=None, add=None, inplace=False):
     say("%s: kind=%s order=%s grid=%s frames=%s x=%s w=%s bias=%s out=%s" % (
         name, kind, order, grid if len(grid) <= 4 else "%d items" % len(grid), frames if frames is None or len(frames) <= 4 else "...",
         tuple(x.shape), tuple(w.shape), b is not None, out_dtype))
     out_dtype = out_dtype or w.dtype
     mod = pe.PatchEmbed(w.to(DEV), b.to(DEV) if b is not None else None, order=order, out_dtype=out_dtype)
-    out = mod(x.to(DEV), grid, frames, kind=kind)
+    if add is None:
+        out = mod(x.to(DEV), grid, frames, kind=kind)
+    else:
+        add_dev = add.to(DEV).contiguous()
+        out = mod(x.to(DEV), grid, frames, kind=kind, add=add_dev, out=add_dev if inplace else None)
     torch.cuda.synchronize()
     if rows is not None:
         got = out[torch.as_tensor(rows, device=DEV)].float().cpu().double().numpy()
@@ -61,7 +65,7 @@ def run(pe, name, x, w, b, grid, frames=None, kind="frames", order="raster", out
         got = out.float().cpu().double().numpy()
     cast = None if x.dtype == w.dtype else {torch.bfloat16: "bf16", torch.float32: "f32"}[w.dtype]
     ref = oracle.forward(x, w, b, grid=grid, frames=frames, kind=kind, order=order, rows=rows,
-                         cast_input_to=cast)
+                         cast_input_to=cast, addend=add)
     mod.close()
     return got, ref, out_dtype
 
@@ -330,6 +334,42 @@ def test_mixed_frame_sizes(pe, case):
     got, ref, od = run(pe, "mixed_" + case, x, w, b, grid, [F for (*_, F) in items], order=order,
                        out_dtype=torch.bfloat16, rows=rows)
     check(got, ref, od, "mixed " + case)
+
+
+ADD_CASES = {
+    # name: (kind, items [(t, h, w, F)] or rows N, weight dtype, out dtype, bias, in place)
+    "image_splitk": ("frames", [(1, 16, 64, 1)], torch.bfloat16, torch.bfloat16, True, False),
+    "images_256x128": ("frames", [(1, 32, 32, 1)] * 4, torch.bfloat16, torch.bfloat16, False, False),
+    "rows_256x256": ("patches", 20000, torch.bfloat16, torch.bfloat16, True, False),
+    "video_f32_out": ("frames", [(2, 8, 10, 4)], torch.bfloat16, torch.float32, True, False),
+    "f32_weights": ("frames", [(1, 10, 12, 1), (1, 6, 4, 1)], torch.float32, torch.float32, True, False),
+    "in_place": ("frames", [(1, 12, 20, 1)], torch.bfloat16, torch.bfloat16, True, True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ADD_CASES))
+def test_forward_add(pe, case):
+    """pe_forward_add: the PatchEmbed plus an [N, E] addend in output row order, added in fp32
+    before the single rounding; the oracle adds it in fp64."""
+    kind, items, wdt, od, bias, inplace = ADD_CASES[case]
+    P, E = 14, 1280
+    K = 3 * 2 * P * P
+    w = make(1100, (E, 3, 2, P, P), wdt, "uniform", 1 / math.sqrt(K))
+    b = make(1101, (E,), wdt, "uniform", 1 / math.sqrt(K)) if bias else None
+    if kind == "patches":
+        n = items
+        x = make(1102, (n, K), wdt)
+        grid, frames, order = [[1, 1, n]], None, "raster"
+    else:
+        xs = [make(1103 + i, (F, 3, h * P, ww * P), wdt) for i, (t, h, ww, F) in enumerate(items)]
+        x = torch.cat([a_.reshape(-1) for a_ in xs])
+        grid, frames, order = [[t, h, ww] for (t, h, ww, F) in items], [F for (*_, F) in items], "merge"
+        n = sum(t * h * ww for (t, h, ww) in grid)
+    add = make(1110, (n, E), od, "uniform", 0.5)
+    rows = None if n <= 4000 else sampled_rows(n, 41, 500)
+    got, ref, _ = run(pe, "add_" + case, x, w, b, grid, frames, kind=kind, order=order, out_dtype=od,
+                      rows=rows, add=add, inplace=inplace)
+    check(got, ref, od, "add " + case)
 
 
 def test_many_items_split_launches(pe):

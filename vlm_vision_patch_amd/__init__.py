@@ -22,7 +22,7 @@ PE_ORDER_RASTER, PE_ORDER_MERGE_WINDOW = 0, 1
 PE_INPUT_PATCHES, PE_INPUT_FRAMES = 0, 1
 
 # every symbol include/pe.h declares
-EXPORTS = ("pe_create", "pe_forward", "pe_num_rows", "pe_destroy", "pe_last_error")
+EXPORTS = ("pe_create", "pe_forward", "pe_forward_add", "pe_num_rows", "pe_destroy", "pe_last_error")
 
 
 class PEError(RuntimeError):
@@ -52,6 +52,8 @@ def _load():
     lib.pe_create.argtypes = [ctypes.POINTER(pe_config), vp, vp, vp, ctypes.POINTER(vp)]
     lib.pe_forward.restype = ctypes.c_int
     lib.pe_forward.argtypes = [vp, i32, vp, i32, pi32, pi32, i32, vp, vp]
+    lib.pe_forward_add.restype = ctypes.c_int
+    lib.pe_forward_add.argtypes = [vp, i32, vp, i32, pi32, pi32, i32, vp, vp, vp]
     lib.pe_num_rows.restype = i64
     lib.pe_num_rows.argtypes = [pi32, i32]
     lib.pe_destroy.restype = ctypes.c_int
@@ -92,6 +94,13 @@ def pe_forward(handle: int, input_kind: int, input_ptr: int, in_dtype: int, grid
     g, n = _i32_array(grid_thw)
     f = _i32_array(frames)[0] if frames is not None else None
     _check(lib.pe_forward(handle, input_kind, input_ptr, in_dtype, g, f, n // 3, out_ptr, stream))
+
+
+def pe_forward_add(handle: int, input_kind: int, input_ptr: int, in_dtype: int, grid_thw, frames,
+                   addend_ptr: int, out_ptr: int, stream: int | None) -> None:
+    g, n = _i32_array(grid_thw)
+    f = _i32_array(frames)[0] if frames is not None else None
+    _check(lib.pe_forward_add(handle, input_kind, input_ptr, in_dtype, g, f, n // 3, addend_ptr, out_ptr, stream))
 
 
 def pe_num_rows(grid_thw) -> int:
@@ -150,7 +159,9 @@ class PatchEmbed:
             stream = torch.cuda.current_stream(self.device).cuda_stream
             self._h = pe_create(cfg, w.data_ptr(), b.data_ptr() if b is not None else None, stream)
 
-    def __call__(self, x, grid_thw, frames=None, *, kind: str = "frames", out=None, stream=None):
+    def __call__(self, x, grid_thw, frames=None, *, kind: str = "frames", out=None, stream=None, add=None):
+        """out = PatchEmbed(x) (+ add: an [N, E] tensor in the output dtype and row order, fused
+        into the epilogue, e.g. the position embeddings that follow the PatchEmbed)."""
         import torch
         grid = [[int(v) for v in row] for row in (grid_thw.tolist() if hasattr(grid_thw, "tolist") else grid_thw)]
         fr = None
@@ -172,8 +183,16 @@ class PatchEmbed:
         x = x.contiguous()
         if stream is None:
             stream = torch.cuda.current_stream(self.device).cuda_stream
-        pe_forward(self._h, PE_INPUT_PATCHES if kind == "patches" else PE_INPUT_FRAMES, x.data_ptr(),
-                   _dtype_code(x.dtype), grid, fr, out.data_ptr(), stream)
+        ik = PE_INPUT_PATCHES if kind == "patches" else PE_INPUT_FRAMES
+        if add is None:
+            pe_forward(self._h, ik, x.data_ptr(), _dtype_code(x.dtype), grid, fr, out.data_ptr(), stream)
+        else:
+            if (tuple(add.shape) != (n, self.embed_dim) or add.dtype != self.out_dtype or not add.is_contiguous()
+                    or add.device != self.device):
+                raise PEError(PE_ERR_INVALID_ARG, "add must be a contiguous [%d, %d] %s tensor on %s"
+                              % (n, self.embed_dim, self.out_dtype, self.device))
+            pe_forward_add(self._h, ik, x.data_ptr(), _dtype_code(x.dtype), grid, fr, add.data_ptr(),
+                           out.data_ptr(), stream)
         return out
 
     def input_elements(self, grid, frames=None, kind="frames") -> int:

@@ -174,9 +174,14 @@ int pe_destroy(pe_handle h) {
     return PE_OK;
 }
 
-int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
-               const int32_t *grid_thw, const int32_t *frames, int32_t n_items, void *out,
-               void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// pe_forward and pe_forward_add: addend is null for the plain forward
+int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
+                 const int32_t *grid_thw, const int32_t *frames, int32_t n_items, const void *addend,
+                 void *out, void *hip_stream) {
     if (!h) return fail(PE_ERR_INVALID_ARG, "handle is NULL");
     if (n_items < 0) return fail(PE_ERR_INVALID_ARG, "n_items must be >= 0 (got %d)", n_items);
     if (n_items == 0) return PE_OK;
@@ -248,6 +253,7 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
             a.in = static_cast<const char *>(input) + r * K * ies;
             a.in_bytes = (uint32_t)(nr * K * ies);
             a.out = static_cast<char *>(out) + r * E * oes;
+            a.addend = addend ? static_cast<const char *>(addend) + r * E * oes : nullptr;
             a.n_rows = (int32_t)nr;
             a.n_items = 0;
             a.colmajor = (uint64_t)nr * K * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
@@ -282,6 +288,7 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         a.in = static_cast<const char *>(input) + x0 * ies;
         a.in_bytes = (uint32_t)(span * ies);
         a.out = static_cast<char *>(out) + row0[i0] * E * oes;
+        a.addend = addend ? static_cast<const char *>(addend) + row0[i0] * E * oes : nullptr;
         a.n_rows = (int32_t)(row0[i1] - row0[i0]);
         a.n_items = i1 - i0;
         a.colmajor = (uint64_t)span * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
@@ -302,6 +309,23 @@ int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dt
         i0 = i1;
     }
     return PE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
+               const int32_t *grid_thw, const int32_t *frames, int32_t n_items, void *out,
+               void *hip_stream) {
+    return forward_impl(h, input_kind, input, in_dtype, grid_thw, frames, n_items, nullptr, out, hip_stream);
+}
+
+int pe_forward_add(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
+                   const int32_t *grid_thw, const int32_t *frames, int32_t n_items, const void *addend,
+                   void *out, void *hip_stream) {
+    if (n_items > 0 && !addend) return fail(PE_ERR_INVALID_ARG, "addend is NULL");
+    return forward_impl(h, input_kind, input, in_dtype, grid_thw, frames, n_items, addend, out, hip_stream);
 }
 
 }  // extern "C"

@@ -26,6 +26,7 @@ struct FwdArgs {
     const void *wpk;     // packed weight
     const float *bias;   // fp32 [E] or null
     void *out;           // launch output base (row 0 of the launch)
+    const void *addend;  // fused add: [rows, E] in the output dtype at the launch's rows, or null
     uint32_t in_bytes;   // bytes addressable from `in` (buffer range; loads beyond read 0)
     int32_t n_rows;      // output rows in this launch
     int32_t E;

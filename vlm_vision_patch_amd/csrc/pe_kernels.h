@@ -66,6 +66,44 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float v) {
     }
 }
 
+// One 16-byte output chunk at element `elem` of out (16/OSZ values, fp32, bias included): with a
+// fused addend (an [N, E] tensor in the output dtype and row order, e.g. the position embeddings
+// that follow PatchEmbed) its chunk at the same position is added in fp32 first; then one
+// round-to-nearest-even cast and a non-temporal store.
+template <int OSZ>
+__device__ __forceinline__ void store_chunk_r(void *out, bool add, const u32x4 &ad, int64_t elem, float (&v)[16 / OSZ]) {
+    if (add) {
+        if constexpr (OSZ == 2) {
+            const uint32_t d[4] = {ad.x, ad.y, ad.z, ad.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] += __builtin_bit_cast(float, d[i] << 16);
+                v[2 * i + 1] += __builtin_bit_cast(float, d[i] & 0xffff0000u);
+            }
+        } else {
+            const f32x4 af = __builtin_bit_cast(f32x4, ad);
+            v[0] += af.x; v[1] += af.y; v[2] += af.z; v[3] += af.w;
+        }
+    }
+    char *dst = static_cast<char *>(out) + elem * OSZ;
+    if constexpr (OSZ == 2) {
+        u32x4 o;
+        o.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        o.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        o.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
+        o.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
+    } else {
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(dst));
+    }
+}
+template <int OSZ>
+__device__ __forceinline__ void store_chunk(void *out, const void *addend, int64_t elem, float (&v)[16 / OSZ]) {
+    u32x4 ad = u32x4{0u, 0u, 0u, 0u};
+    if (addend) ad = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(addend) + elem * OSZ);
+    store_chunk_r<OSZ>(out, addend != nullptr, ad, elem, v);
+}
+
 // ----------------------------------------------------------------------------------------
 // Weight pre-pack: W[E][C][Tp][P][P] -> packed[s][E'/NB][g][NB][16 bytes] in the fragment order
 // (NB = 32 for bf16, 16 for fp32; columns e >= E are zero). One thread writes one 16-byte
@@ -601,19 +639,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs 
             const float *src = ep + r * EP_PITCH + q * VPC;
             const int row = rbase + r, col = wcol0 + q * VPC;
             if (row < a.n_rows && col < a.E) {
-                char *dst = static_cast<char *>(a.out) + ((int64_t)row * a.E + col) * OSZ;
-                if constexpr (OSZ == 2) {
-                    const f32x4 v0 = *reinterpret_cast<const f32x4 *>(src);
-                    const f32x4 v1 = *reinterpret_cast<const f32x4 *>(src + 4);
-                    u32x4 o;
-                    o.x = (uint32_t)f32_to_bf16_rne(v0.x) | ((uint32_t)f32_to_bf16_rne(v0.y) << 16);
-                    o.y = (uint32_t)f32_to_bf16_rne(v0.z) | ((uint32_t)f32_to_bf16_rne(v0.w) << 16);
-                    o.z = (uint32_t)f32_to_bf16_rne(v1.x) | ((uint32_t)f32_to_bf16_rne(v1.y) << 16);
-                    o.w = (uint32_t)f32_to_bf16_rne(v1.z) | ((uint32_t)f32_to_bf16_rne(v1.w) << 16);
-                    __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
-                } else {
-                    __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(src), reinterpret_cast<f32x4 *>(dst));
-                }
+                float v[VPC];
+#pragma unroll
+                for (int e = 0; e < VPC; ++e) v[e] = src[e];
+                store_chunk<OSZ>(a.out, a.addend, (int64_t)row * a.E + col, v);
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -889,47 +918,61 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     constexpr int RCH = TN * 32 / VPC;            // chunks per row
     constexpr int CHUNKS = 16 * RCH;              // chunks in 16 rows
     const int wcol0 = col0 + wn * TN * 32;
+    // A fused bf16 addend is read one 16-row block ahead, so its latency overlaps the staging and
+    // the stores of the block before; an fp32 one (twice the registers) is read at the start of its
+    // own block and overlaps that block's staging. Chunks outside the output read the addend's
+    // first chunk.
+    constexpr int CPL = (CHUNKS + 63) / 64;       // chunks per lane in 16 rows
+    constexpr int NBLK = 2 * TM;                  // 16-row blocks per wave
+    constexpr int NBUF = OSZ == 2 ? 2 : 1;
+    const bool has_add = a.addend != nullptr;
+    auto add_load = [&](int it, u32x4 (&dst)[CPL]) {
 #pragma unroll
-    for (int rb = 0; rb < TM; ++rb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-            for (int cb = 0; cb < TN; ++cb)
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int i = half * 8 + q;
-                    const int rl = 8 * (q / 4) + 4 * h + (q % 4);   // row within these 16
-                    ep[rl * EP_PITCH + cb * 32 + l32] = acc[rb][cb][i];
-                }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are in LDS
-            __builtin_amdgcn_wave_barrier();
-            const int rbase = row0 + (wm * TM + rb) * 32 + half * 16;
-#pragma unroll
-            for (int jj = 0; jj < (CHUNKS + 63) / 64; ++jj) {
-                const int c = jj * 64 + lane;
-                if (CHUNKS % 64 != 0 && c >= CHUNKS) break;
-                const int r = c / RCH, qq = c % RCH;
-                const float *src = ep + r * EP_PITCH + qq * VPC;
-                const int row = rbase + r, col = wcol0 + qq * VPC;
-                if (row < a.n_rows && col < a.E) {
-                    char *dst = static_cast<char *>(a.out) + ((int64_t)row * a.E + col) * OSZ;
-                    if constexpr (OSZ == 2) {
-                        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(src);
-                        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(src + 4);
-                        u32x4 o;
-                        o.x = (uint32_t)f32_to_bf16_rne(v0.x) | ((uint32_t)f32_to_bf16_rne(v0.y) << 16);
-                        o.y = (uint32_t)f32_to_bf16_rne(v0.z) | ((uint32_t)f32_to_bf16_rne(v0.w) << 16);
-                        o.z = (uint32_t)f32_to_bf16_rne(v1.x) | ((uint32_t)f32_to_bf16_rne(v1.y) << 16);
-                        o.w = (uint32_t)f32_to_bf16_rne(v1.z) | ((uint32_t)f32_to_bf16_rne(v1.w) << 16);
-                        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
-                    } else {
-                        __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(src), reinterpret_cast<f32x4 *>(dst));
-                    }
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
+        for (int jj = 0; jj < CPL; ++jj) {
+            const int c = jj * 64 + lane;
+            const int r = c / RCH, qq = c % RCH;
+            const int row = row0 + (wm * TM + it / 2) * 32 + (it % 2) * 16 + r, col = wcol0 + qq * VPC;
+            const bool ok = (CHUNKS % 64 == 0 || c < CHUNKS) && row < a.n_rows && col < a.E;
+            dst[jj] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.addend) +
+                                                       (ok ? ((int64_t)row * a.E + col) * OSZ : 0));
         }
+    };
+    u32x4 adq[NBUF][CPL];
+    if (NBUF == 2 && has_add) add_load(0, adq[0]);
+#pragma unroll
+    for (int it = 0; it < NBLK; ++it) {
+        const int rb = it / 2, half = it % 2;
+        if (has_add) {
+            if (NBUF == 1) add_load(it, adq[0]);
+            else if (it + 1 < NBLK) add_load(it + 1, adq[(it + 1) % NBUF]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < TN; ++cb)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int i = half * 8 + q;
+                const int rl = 8 * (q / 4) + 4 * h + (q % 4);   // row within these 16
+                ep[rl * EP_PITCH + cb * 32 + l32] = acc[rb][cb][i];
+            }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int rbase = row0 + (wm * TM + rb) * 32 + half * 16;
+#pragma unroll
+        for (int jj = 0; jj < CPL; ++jj) {
+            const int c = jj * 64 + lane;
+            if (CHUNKS % 64 != 0 && c >= CHUNKS) break;
+            const int r = c / RCH, qq = c % RCH;
+            const float *src = ep + r * EP_PITCH + qq * VPC;
+            const int row = rbase + r, col = wcol0 + qq * VPC;
+            if (row < a.n_rows && col < a.E) {
+                float v[VPC];
+#pragma unroll
+                for (int e = 0; e < VPC; ++e) v[e] = src[e];
+                store_chunk_r<OSZ>(a.out, has_add, adq[it % NBUF][jj], (int64_t)row * a.E + col, v);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -1076,17 +1119,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
                     t += *reinterpret_cast<const f32x4 *>(p0 + w * (PART / 4) + r * PITCH + q * VPC + e4);
                 v[e4] = t.x; v[e4 + 1] = t.y; v[e4 + 2] = t.z; v[e4 + 3] = t.w;
             }
-            char *dst = static_cast<char *>(a.out) + ((int64_t)row * a.E + col) * OSZ;
-            if constexpr (OSZ == 2) {
-                u32x4 o;
-                o.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
-                o.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-                o.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
-                o.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
-                __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
-            } else {
-                __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(dst));
-            }
+            store_chunk<OSZ>(a.out, a.addend, (int64_t)row * a.E + col, v);
         }
     }
 }
