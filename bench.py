@@ -162,6 +162,75 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
                 stats=stats, cold_ms=cold_ms)
 
 
+def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6):
+    """The PatchMerger front end on the workload's output rows: pe_layernorm over [N, E] in the
+    output dtype (synthetic rows and parameters), alone and after the PatchEmbed as one step
+    (PatchEmbed, then the LayerNorm in place). Graph of K steps, median of `reps` replays."""
+    import torch
+    import workloads
+    import vlm_vision_patch_amd as pe
+
+    wl = workloads.WORKLOADS[idx]
+    dev = torch.device("cuda:0")
+    odt = workloads.DTYPES[wl.out_dtype]
+    n = sum(t * h * w for (t, h, w) in wl.grid)
+    E = wl.embed
+    rows = (workloads.random_tensor((n, E), seed=4000 + idx) * 0.6).to(odt).to(dev)
+    y = torch.empty_like(rows)
+    gam = (1.0 + 0.1 * workloads.random_tensor((E,), seed=4100 + idx)).to(odt).to(dev)
+    bet = (0.1 * workloads.random_tensor((E,), seed=4200 + idx)).to(odt).to(dev)
+    x, w, b = workloads.generate(wl)
+    x, w = x.to(dev), w.to(dev)
+    b = b.to(dev) if b is not None else None
+    mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=odt)
+    grid, frames = [list(g) for g in wl.grid], list(wl.frames) or None
+    out = torch.empty((n, E), dtype=odt, device=dev)
+    s = torch.cuda.Stream(device=dev)
+
+    def ln_only():
+        pe.layer_norm(rows, gam, bet, eps, out=y, stream=s.cuda_stream)
+
+    def pipeline():
+        mod(x, grid, frames, out=out, stream=s.cuda_stream)
+        pe.layer_norm(out, gam, bet, eps, out=out, stream=s.cuda_stream)
+
+    res = {}
+    for name, fn in (("layernorm", ln_only), ("patch_embed_then_layernorm", pipeline)):
+        with torch.cuda.stream(s):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(steps):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            per = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                g.replay()
+                e1.record(s)
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) / steps)
+            del g
+        per.sort()
+        res[name] = per[len(per) // 2]
+    mod.close()
+    esz = rows.element_size()
+    ln_bytes = 2 * n * E * esz + 2 * E * esz
+    ln_ms = res["layernorm"]
+    return {"what": "LayerNorm over E of the [N, E] %s rows (the PatchMerger front end; in merge-window "
+                    "order the 2x2 concatenation is a view)" % wl.out_dtype,
+            "n_rows": n, "embed": E, "ms_per_step": round(ln_ms, 5),
+            "alg_bytes": ln_bytes, "gbs": round(ln_bytes / (ln_ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(ln_bytes / (ln_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "patch_embed_then_layernorm_ms": round(res["patch_embed_then_layernorm"], 5),
+            "patch_embed_then_layernorm_patches_per_s": round(n / (res["patch_embed_then_layernorm"] / 1e3), 1),
+            "steps": steps}
+
+
 def time_linear_context(idx, steps=20):
     """hipBLASLt (torch.nn.functional.linear) on the same product with the patches already
     flattened into a contiguous [N, K] matrix: context for the gather-fused kernel, not a target."""
@@ -247,10 +316,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--extra", type=str, default="5,5r,5a,5s8,4,6,1",
+    ap.add_argument("--extra", type=str, default="5,5r,5a,5n,5s8,4,6,1",
                     help="comma-separated further workloads reported under 'also' ('' for none); "
                          "a trailing r feeds that workload's patches as pre-flattened rows, a trailing "
-                         "a fuses the add of an [N, E] tensor; sN keeps its first N items (one GPU's "
+                         "a fuses the add of an [N, E] tensor, a trailing n times the PatchMerger "
+                         "LayerNorm on its output rows; sN keeps its first N items (one GPU's "
                          "share of an N-way item split)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the library-GEMM context line (hipBLASLt on the same product)")
@@ -303,6 +373,10 @@ def main():
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     also = {}
     for spec in [v.strip() for v in args.extra.split(",") if v.strip()]:
+        if spec.endswith("n"):
+            e = int(spec[:-1])
+            also[workloads_name(e) + "_merger_layernorm"] = time_merger_front(e, max(5, min(args.steps, 50)))
+            continue
         as_rows = spec.endswith("r")
         with_add = spec.endswith("a")
         share = int(spec.split("s")[1]) if "s" in spec else None

@@ -134,6 +134,31 @@ int pe_forward_add(pe_handle h, int32_t input_kind, const void *input, int32_t i
                    const int32_t *grid_thw, const int32_t *frames, int32_t n_items, const void *addend,
                    void *out, void *hip_stream);
 
+/*
+ * pe_layernorm -- y[r, :] = (x[r, :] - mean_r) / sqrt(var_r + eps) * gamma + beta, for every row r
+ *   of a row-major [n_rows, dim] tensor, asynchronously on hip_stream, on the current device.
+ *   The PatchMerger after the vision tower starts with a LayerNorm over E and then concatenates
+ *   the 2x2 neighbouring patches into one 4E row ("freechatgpt/mytransformer", the vision
+ *   encoder diagram in section 3.2 and the PatchMerger bullet in section 4.1). On rows that
+ *   pe_forward wrote in PE_ORDER_MERGE_WINDOW order with m = 2, y viewed as [n_rows / 4, 4 * dim]
+ *   is that concatenation, so this call is the whole front end of the merger.
+ *   x, y       device [n_rows, dim] in dtype (pe_dtype). y may be x (in place); otherwise the two
+ *              must not overlap. 16-byte aligned.
+ *   gamma,beta device [dim] in param_dtype (pe_dtype), 16-byte aligned, or NULL for all ones /
+ *              all zeros.
+ *   eps        finite, >= 0 (the pages give no value; the Python binding defaults to 1e-6). With
+ *              eps = 0 a constant row gives NaN, as the formula does.
+ *   n_rows     >= 0; 0 is a no-op that returns PE_OK.
+ *   dim        a positive multiple of 8, at most 4096.
+ * Arithmetic: mean_r and the biased variance var_r = mean((x - mean_r)^2) in fp32 (the pages
+ * compute the language model's norms in fp32 for stability, section 3.3; the same is taken here),
+ * y in fp32, one round-to-nearest-even cast to dtype. Allocates nothing.
+ * Returns PE_OK, PE_ERR_INVALID_ARG (NULL x/y, bad dtype, bad eps, misalignment, partial
+ * overlap), PE_ERR_UNSUPPORTED (dim), PE_ERR_SHAPE (byte count overflow) or PE_ERR_HIP.
+ */
+int pe_layernorm(const void *x, int32_t dtype, const void *gamma, const void *beta, int32_t param_dtype,
+                 float eps, int64_t n_rows, int32_t dim, void *y, void *hip_stream);
+
 /* N = sum over items of t*h*w ("freechatgpt/mytransformer" section 3.2: N = t*h*w), or a
  * negative pe_status for a NULL grid, negative n_items or a non-positive entry. */
 int64_t pe_num_rows(const int32_t *grid_thw, int32_t n_items);

@@ -4,9 +4,10 @@ Only the test suite, the smoke check and the benchmark's CPU-baseline leg may im
 package. The product path (the HIP library and its Python binding) never loads it and shares
 no code with it.
 
-The arithmetic lives in ``pe_oracle.c`` (plain C, fp64, a direct five-loop Conv3d per output
-row; its header states the definition and the passages of the pages it follows). This module
-compiles it with gcc on first use, converts inputs to fp64 exactly and calls it via ctypes.
+The PatchEmbed arithmetic lives in ``pe_oracle.c`` (plain C, fp64, a direct five-loop Conv3d per
+output row; its header states the definition and the passages of the pages it follows). This
+module compiles it with gcc on first use, converts inputs to fp64 exactly and calls it via
+ctypes. The PatchMerger front end (``layer_norm``, ``merger_front``) is plain numpy in fp64.
 
 Parity pins for every function here are in ``tests/test_oracle.py``.
 """
@@ -156,3 +157,34 @@ def forward(x, w, b=None, *, grid, frames=None, kind="frames", order="raster", m
         ad = _f64(addend).reshape(-1, E)
         out += ad[rr] if rr is not None else ad
     return out
+
+
+def layer_norm(x, gamma=None, beta=None, eps=1e-6):
+    """LayerNorm over the last dimension, in fp64, from its definition: per row the mean, the
+    biased variance (mean of the squared deviations), then (x - mean) / sqrt(var + eps) * gamma
+    + beta. It opens the PatchMerger ("freechatgpt/mytransformer", section 3.2's vision encoder
+    diagram and section 4.1's PatchMerger bullet: LayerNorm, then the 2x2 concatenation).
+    gamma / beta None mean ones / zeros. Returns a numpy array shaped like x."""
+    xd = _f64(x)
+    mean = xd.sum(axis=-1, keepdims=True) / xd.shape[-1]
+    dev = xd - mean
+    var = (dev * dev).sum(axis=-1, keepdims=True) / xd.shape[-1]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = dev / np.sqrt(var + eps)
+    if gamma is not None:
+        y = y * _f64(gamma)
+    if beta is not None:
+        y = y + _f64(beta)
+    return y
+
+
+def merger_front(rows, gamma=None, beta=None, eps=1e-6, m=2):
+    """The PatchMerger's LayerNorm and m x m concatenation: rows [N, E] in merge-window order
+    (the m*m patches of each window consecutive) -> [N / m^2, m^2 * E], row j holding the
+    normalized patches of window j side by side in their window order (the section 3.2 diagram
+    of "freechatgpt/mytransformer": 2x2 neighbours joined into 1280 x 4 = 5120)."""
+    y = layer_norm(rows, gamma, beta, eps)
+    n, e = y.shape
+    if n % (m * m):
+        raise ValueError("row count %d is not a multiple of %d" % (n, m * m))
+    return y.reshape(n // (m * m), m * m * e)

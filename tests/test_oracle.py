@@ -12,7 +12,9 @@ The oracle is checked against what the pages and the mathematics fix, never agai
   * integer inputs give exactly the integer product (that page's R1 == R2 check);
   * row order against the position ids printed on the "Qwen2.5VL语言模型" page and the 2x2
     concatenation of the PatchMerger ("freechatgpt/mytransformer" section 3.2);
-  * the shape facts printed on the mytransformer and "patch详解" pages.
+  * the shape facts printed on the mytransformer and "patch详解" pages;
+  * the PatchMerger front end: LayerNorm against hand values, torch's float64 layer_norm and its
+    invariants; the 2x2 concatenation against raster rows gathered by window.
 """
 import math
 
@@ -362,3 +364,72 @@ def test_merge_order_within_window_reading():
     raster_of_row = (pos[:, 1] * h + pos[:, 2]) * w + pos[:, 3]
     want = np.arange(t * h * w).reshape(t, h // 2, 2, w // 2, 2).transpose(0, 1, 3, 2, 4)
     assert np.array_equal(raster_of_row, want.reshape(-1))
+
+
+# ---------------------------------------------------------------------------------------------
+# PatchMerger front end: LayerNorm over E, then the 2x2 concatenation ("freechatgpt/mytransformer"
+# section 3.2's vision encoder diagram and section 4.1's PatchMerger bullet)
+# ---------------------------------------------------------------------------------------------
+
+def test_layer_norm_hand_values():
+    """Row (1, 2, 3, 4): mean 5/2 and biased variance 5/4, so with eps = 0 the row normalizes to
+    (-3, -1, 1, 3) / sqrt(5). With eps = 3/4 the root is sqrt(2). The affine step scales by gamma
+    and shifts by beta per column. (An unbiased variance, a dropped eps or a sign slip each fail
+    one of these.)"""
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    y = oracle.layer_norm(x, eps=0.0)
+    assert np.allclose(y, np.array([[-3.0, -1.0, 1.0, 3.0]]) / math.sqrt(5.0), rtol=0, atol=1e-15)
+    y = oracle.layer_norm(x, eps=0.75)
+    assert np.allclose(y, np.array([[-1.5, -0.5, 0.5, 1.5]]) / math.sqrt(2.0), rtol=0, atol=1e-15)
+    y = oracle.layer_norm(x, gamma=[2.0, 1.0, -1.0, 0.5], beta=[1.0, 0.0, 0.25, -2.0], eps=0.0)
+    want = np.array([-3.0 * 2, -1.0, -1.0, 3.0 * 0.5]) / math.sqrt(5.0) + np.array([1.0, 0.0, 0.25, -2.0])
+    assert np.allclose(y[0], want, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("E,eps", [(1280, 1e-6), (1024, 1e-5), (1152, 1e-6), (8, 1e-3)])
+def test_layer_norm_matches_torch_f64(E, eps):
+    """Library routine: torch.nn.functional.layer_norm in float64 on the CPU."""
+    g = torch.Generator().manual_seed(E)
+    x = torch.randn(37, E, generator=g, dtype=torch.float64) * 0.7 + 0.3
+    gam = torch.randn(E, generator=g, dtype=torch.float64)
+    bet = torch.randn(E, generator=g, dtype=torch.float64)
+    want = torch.nn.functional.layer_norm(x, (E,), gam, bet, eps).numpy()
+    got = oracle.layer_norm(x, gam, bet, eps)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_norm_invariants():
+    """Each normalized row (gamma 1, beta 0, eps 0) has mean 0 and mean square 1; the result is
+    unchanged by x -> a*x + c for a > 0 and negated for a < 0; a constant row gives beta."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((16, 1280)) * 3.0 + 7.0
+    y = oracle.layer_norm(x, eps=0.0)
+    assert np.abs(y.mean(axis=1)).max() < 1e-12
+    assert np.abs((y * y).mean(axis=1) - 1.0).max() < 1e-12
+    np.testing.assert_allclose(oracle.layer_norm(2.5 * x - 4.0, eps=0.0), y, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(oracle.layer_norm(-0.5 * x + 1.0, eps=0.0), -y, rtol=0, atol=1e-11)
+    beta = rng.standard_normal(1280)
+    c = np.full((3, 1280), 0.3125)
+    assert np.array_equal(oracle.layer_norm(c, rng.standard_normal(1280), beta, 1e-6), np.tile(beta, (3, 1)))
+
+
+def test_merger_front_concatenates_2x2_neighbours():
+    """merger_front on merge-window rows: row j of the [N/4, 4E] result is the LayerNorm of the
+    four patches of window j, side by side. Checked against raster rows (the Conv3d view order)
+    gathered by window coordinates: window (t, i, j) holds patches (t, 2i + dh, 2j + dw)."""
+    gen = torch.Generator().manual_seed(11)
+    P, E, t, h, w = 14, 24, 2, 4, 6
+    frames = torch.randn(2 * t, 3, h * P, w * P, generator=gen).to(torch.bfloat16)
+    wt = (torch.randn(E, 3, 2, P, P, generator=gen) * 0.03).to(torch.bfloat16)
+    b = (torch.randn(E, generator=gen) * 0.1).to(torch.bfloat16)
+    gam = torch.randn(E, generator=gen, dtype=torch.float64)
+    bet = torch.randn(E, generator=gen, dtype=torch.float64)
+    raster = oracle.forward(frames, wt, b, grid=[[t, h, w]], frames=[2 * t], order="raster")
+    merge = oracle.forward(frames, wt, b, grid=[[t, h, w]], frames=[2 * t], order="merge", m=2)
+    got = oracle.merger_front(merge, gam, bet, 1e-6, m=2)
+    assert got.shape == (t * h * w // 4, 4 * E)
+    ln_r = oracle.layer_norm(raster, gam, bet, 1e-6).reshape(t, h, w, E)
+    want = ln_r.reshape(t, h // 2, 2, w // 2, 2, E).transpose(0, 1, 3, 2, 4, 5).reshape(-1, 4 * E)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # the merged token count of the mytransformer shape table: [1944, 1280] rows -> 486 tokens
+    assert oracle.merger_front(np.ones((1944, 8)) * np.arange(8), m=2).shape == (486, 32)

@@ -22,7 +22,8 @@ PE_ORDER_RASTER, PE_ORDER_MERGE_WINDOW = 0, 1
 PE_INPUT_PATCHES, PE_INPUT_FRAMES = 0, 1
 
 # every symbol include/pe.h declares
-EXPORTS = ("pe_create", "pe_forward", "pe_forward_add", "pe_num_rows", "pe_destroy", "pe_last_error")
+EXPORTS = ("pe_create", "pe_forward", "pe_forward_add", "pe_layernorm", "pe_num_rows", "pe_destroy",
+           "pe_last_error")
 
 
 class PEError(RuntimeError):
@@ -54,6 +55,8 @@ def _load():
     lib.pe_forward.argtypes = [vp, i32, vp, i32, pi32, pi32, i32, vp, vp]
     lib.pe_forward_add.restype = ctypes.c_int
     lib.pe_forward_add.argtypes = [vp, i32, vp, i32, pi32, pi32, i32, vp, vp, vp]
+    lib.pe_layernorm.restype = ctypes.c_int
+    lib.pe_layernorm.argtypes = [vp, i32, vp, vp, i32, ctypes.c_float, i64, i32, vp, vp]
     lib.pe_num_rows.restype = i64
     lib.pe_num_rows.argtypes = [pi32, i32]
     lib.pe_destroy.restype = ctypes.c_int
@@ -101,6 +104,11 @@ def pe_forward_add(handle: int, input_kind: int, input_ptr: int, in_dtype: int, 
     g, n = _i32_array(grid_thw)
     f = _i32_array(frames)[0] if frames is not None else None
     _check(lib.pe_forward_add(handle, input_kind, input_ptr, in_dtype, g, f, n // 3, addend_ptr, out_ptr, stream))
+
+
+def pe_layernorm(x_ptr: int, dtype: int, gamma_ptr: int | None, beta_ptr: int | None, param_dtype: int,
+                 eps: float, n_rows: int, dim: int, y_ptr: int, stream: int | None) -> None:
+    _check(lib.pe_layernorm(x_ptr, dtype, gamma_ptr, beta_ptr, param_dtype, eps, n_rows, dim, y_ptr, stream))
 
 
 def pe_num_rows(grid_thw) -> int:
@@ -215,3 +223,35 @@ class PatchEmbed:
             self.close()
         except Exception:
             pass
+
+
+def layer_norm(x, gamma=None, beta=None, eps: float = 1e-6, *, out=None, stream=None):
+    """LayerNorm over the last dimension of a contiguous [..., dim] bf16 / fp32 device tensor
+    (pe_layernorm): the front of the PatchMerger. ``out`` may be ``x`` (in place). On PatchEmbed
+    rows in merge-window order (m = 2), ``layer_norm(rows).view(-1, 4 * dim)`` is the merger's
+    2x2 concatenation of normalized rows."""
+    import torch
+    if not x.is_cuda or not x.is_contiguous() or x.dim() < 1:
+        raise PEError(PE_ERR_INVALID_ARG, "x must be a contiguous device tensor")
+    dim = int(x.shape[-1])
+    n_rows = x.numel() // dim if dim else 0
+    pdt = None
+    for p in (gamma, beta):
+        if p is not None:
+            if (tuple(p.shape) != (dim,) or not p.is_contiguous() or p.device != x.device
+                    or (pdt is not None and p.dtype != pdt)):
+                raise PEError(PE_ERR_INVALID_ARG, "gamma / beta must be contiguous [%d] tensors of one dtype "
+                              "on %s" % (dim, x.device))
+            pdt = p.dtype
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise PEError(PE_ERR_INVALID_ARG, "out must be a contiguous tensor like x")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        pe_layernorm(x.data_ptr(), _dtype_code(x.dtype), gamma.data_ptr() if gamma is not None else None,
+                     beta.data_ptr() if beta is not None else None,
+                     _dtype_code(pdt) if pdt is not None else _dtype_code(x.dtype), float(eps), n_rows, dim,
+                     out.data_ptr(), stream)
+    return out

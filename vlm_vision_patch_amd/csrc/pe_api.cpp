@@ -2,6 +2,7 @@
 // launch plan of pe_forward (item tables, launch splitting). No allocation after pe_create.
 #include "pe.h"
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -326,6 +327,30 @@ int pe_forward_add(pe_handle h, int32_t input_kind, const void *input, int32_t i
                    void *out, void *hip_stream) {
     if (n_items > 0 && !addend) return fail(PE_ERR_INVALID_ARG, "addend is NULL");
     return forward_impl(h, input_kind, input, in_dtype, grid_thw, frames, n_items, addend, out, hip_stream);
+}
+
+int pe_layernorm(const void *x, int32_t dtype, const void *gamma, const void *beta, int32_t param_dtype,
+                 float eps, int64_t n_rows, int32_t dim, void *y, void *hip_stream) {
+    if (n_rows < 0) return fail(PE_ERR_INVALID_ARG, "n_rows must be >= 0 (got %lld)", (long long)n_rows);
+    if (!dtype_ok(dtype) || !dtype_ok(param_dtype))
+        return fail(PE_ERR_INVALID_ARG, "dtype %d / param_dtype %d is not a pe_dtype", dtype, param_dtype);
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(PE_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (dim <= 0 || dim % 8 != 0 || dim > pe::kNormMaxDim)
+        return fail(PE_ERR_UNSUPPORTED, "dim %d: a positive multiple of 8 up to %d is supported", dim, pe::kNormMaxDim);
+    if (n_rows == 0) return PE_OK;
+    if (!x || !y) return fail(PE_ERR_INVALID_ARG, "x or y is NULL");
+    const int es = esize(dtype);
+    if (n_rows > INT64_MAX / ((int64_t)dim * es)) return fail(PE_ERR_SHAPE, "n_rows * dim overflows");
+    const uintptr_t al = (uintptr_t)x | (uintptr_t)y | (uintptr_t)gamma | (uintptr_t)beta;
+    if (al & 15) return fail(PE_ERR_INVALID_ARG, "x, y, gamma and beta must be 16-byte aligned");
+    const uintptr_t bytes = (uintptr_t)(n_rows * dim * es);
+    const uintptr_t xb = (uintptr_t)x, yb = (uintptr_t)y;
+    if (xb != yb && xb < yb + bytes && yb < xb + bytes)
+        return fail(PE_ERR_INVALID_ARG, "y overlaps x without being x");
+    hipError_t e = pe::launch_layernorm(x, es, y, gamma, beta, esize(param_dtype), eps, n_rows, dim,
+                                        static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "layernorm launch");
+    return PE_OK;
 }
 
 }  // extern "C"

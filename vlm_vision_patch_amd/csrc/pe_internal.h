@@ -183,4 +183,10 @@ hipError_t launch_forward_p16_bf16in(const FwdArgs &a, int out_esz, hipStream_t 
 hipError_t launch_forward_p14_f32in(const FwdArgs &a, int w_esz, int out_esz, hipStream_t st);
 hipError_t launch_forward_p16_f32in(const FwdArgs &a, int w_esz, int out_esz, hipStream_t st);
 
+// LayerNorm over the last dimension of [n_rows, dim] (pe_norm.hip). esz: bytes of an x / y element
+// (2 bf16, 4 fp32), psz: of a gamma / beta element; gamma / beta may be null (1 / 0).
+constexpr int kNormMaxDim = 4096;
+hipError_t launch_layernorm(const void *x, int esz, void *y, const void *gamma, const void *beta, int psz,
+                            float eps, int64_t n_rows, int dim, hipStream_t st);
+
 }  // namespace pe
