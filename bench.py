@@ -70,14 +70,16 @@ def dominant_kernel(wl, num_cus=256):
     return "pe_fwd32_kernel" if min(c256, c128) <= csk else "pe_fwd32_sk_kernel"
 
 
-def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=10, cold=False, add=False):
+def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=10, cold=False, add=False,
+                  fold=False):
     """rows: feed the workload's patches as pre-flattened rows [N, K] (the processor's
     pixel_values layout) instead of its frames: same N, weight and bias, synthetic N(0, 1) rows.
     items: keep only the first `items` items (one GPU's share of an item split).
     The graph of K steps is replayed `reps` times, each replay timed: median, p10 and p90 per step.
     cold: also time single launches after overwriting a 1 GiB buffer (L2 and the 256 MB
     Infinity Cache hold nothing of the inputs), median of `reps`.
-    add: fuse the add of a synthetic [N, E] tensor (position embeddings) into the epilogue."""
+    add: fuse the add of a synthetic [N, E] tensor (position embeddings) into the epilogue.
+    fold: the approximate image-fold mode (single-frame items on W[:, :, 0] + W[:, :, 1] in bf16)."""
     import torch
     import workloads
     import vlm_vision_patch_amd as pe
@@ -96,7 +98,7 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
         kind, grid, frames = "patches", [[1, 1, n]], None
     x, w = x.to(dev), w.to(dev)
     b = b.to(dev) if b is not None else None
-    mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype])
+    mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype], image_fold=fold)
     out = torch.empty((n, wl.embed), dtype=workloads.DTYPES[wl.out_dtype], device=dev)
     addend = None
     if add:
@@ -316,12 +318,12 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--extra", type=str, default="5,5r,5a,5n,5s8,4,6,1",
+    ap.add_argument("--extra", type=str, default="5,5r,5a,5n,5f,2f,5s8,4,6,1",
                     help="comma-separated further workloads reported under 'also' ('' for none); "
                          "a trailing r feeds that workload's patches as pre-flattened rows, a trailing "
                          "a fuses the add of an [N, E] tensor, a trailing n times the PatchMerger "
-                         "LayerNorm on its output rows; sN keeps its first N items (one GPU's "
-                         "share of an N-way item split)")
+                         "LayerNorm on its output rows, a trailing f runs the approximate image-fold "
+                         "mode; sN keeps its first N items (one GPU's share of an N-way item split)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the library-GEMM context line (hipBLASLt on the same product)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -379,19 +381,25 @@ def main():
             continue
         as_rows = spec.endswith("r")
         with_add = spec.endswith("a")
+        fold = spec.endswith("f")
         share = int(spec.split("s")[1]) if "s" in spec else None
-        e = int(spec.rstrip("ra").split("s")[0])
-        if e == args.workload and not as_rows and share is None:
+        e = int(spec.rstrip("raf").split("s")[0])
+        if e == args.workload and not as_rows and share is None and not fold:
             continue
         st = max(5, min(args.steps, 50))
-        q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows, items=share, reps=3, add=with_add)
+        q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows, items=share, reps=3, add=with_add,
+                          fold=fold)
         qt = q["ms"] / 1e3
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
-        also[q["wl"].name + ("_as_patch_rows" if as_rows else "") + ("_plus_pos_embed" if with_add else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
+        also[q["wl"].name + ("_as_patch_rows" if as_rows else "") + ("_plus_pos_embed" if with_add else "")
+             + ("_image_fold_approx" if fold else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
                               "tflops": round(q["flops"] / qt / 1e12, 2),
                               "frac_matrix_peak": round(q["flops"] / qt / 1e12 / qpk, 4),
                               "frac_hbm": round(q["bytes"] / qt / 1e9 / PEAK_HBM_GBS, 4),
-                              "n_patches": q["n"], "steps": st}
+                              "n_patches": q["n"], "steps": st,
+                              **({"approximate": "image fold: W[:, :, 0] + W[:, :, 1] rounded to bf16 once; "
+                                                 "tflops counts the nominal Conv3d FLOPs, the matrix cores do "
+                                                 "about half for images"} if fold else {})}
     if not args.no_context and not args.eager:
         also["context_library_gemm_" + workloads_name(5)] = time_linear_context(5)
     cpu = None if args.no_cpu else cpu_baseline(args.workload)

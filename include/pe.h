@@ -65,7 +65,17 @@ typedef struct {
     int32_t weight_dtype;         /* pe_dtype of weight and bias.                            */
     int32_t out_dtype;            /* pe_dtype of the output.                                 */
     int32_t out_order;            /* pe_order, applied to FRAMES input.                      */
+    int32_t image_fold;           /* 0: exact (default). 1: APPROXIMATE mode for single-frame   */
+                                  /* items, see below. Needs a bf16 weight.                   */
 } pe_config;
+
+/* image_fold. An image item repeats its one frame in both temporal slots, so its output is
+ * x . (W[:, :, 0] + W[:, :, 1]) over the C*P*P elements of that frame (the per-temporal-slice sum of
+ * the Conv3d -> Conv2d decomposition on "Optimize VLM PatchEmbed"). With image_fold = 1, pe_create
+ * also packs that folded weight, rounded to bf16 once, and frames launches of single-frame items
+ * use it: half the matrix-core work. Approximate: the folded weight's rounding (at most 2^-8 of
+ * |W0 + W1| per element) adds up to 2^-8 * sum_k |x_k| |W0_k + W1_k| to each output, beyond the exact
+ * path's single output rounding. Video items and patch rows are unaffected (exact). */
 
 typedef struct pe_handle_s *pe_handle;
 

@@ -81,6 +81,38 @@ static int check_rows(int P) {
     return 0;
 }
 
+// The folded image map: fold pair p = 2s + j of k-step s; its halves are unique fragments of one
+// load kind (or the second half empty); every element of one frame (C*P*P) exactly once.
+static int check_fold(int P) {
+    using namespace pe;
+    const int rows = kC * P, S = fold_steps(P);
+    std::vector<int> hits(rows * P, 0);
+    int pads = 0;
+    for (int p = 0; p < 2 * S; ++p) {
+        const FoldPair fp = fold_pair(P, p);
+        if (fp.uf0 < 0 || fp.uf0 >= 2 * tt_steps(P)) { printf("fold pair %d: bad first fragment\n", p); return 1; }
+        if (fp.uf1 >= 0 && tt_frag(P, fp.uf1).kind != tt_frag(P, fp.uf0).kind) {
+            printf("fold pair %d: two load kinds\n", p); return 1;
+        }
+        for (int half = 0; half < 2; ++half) {
+            const int uf = half ? fp.uf1 : fp.uf0;
+            if (uf < 0) { pads += 8; continue; }
+            const UFrag f = tt_frag(P, uf);
+            for (int j = 0; j < 8; ++j) {
+                int u = f.u1, x = f.x1 + j;
+                if (f.kind == kUfSplit62 && j >= 6) { u = f.u2; x = f.x2 + j - 6; }
+                if (f.kind == kUfTail4 && j >= 4) { ++pads; continue; }
+                if (u < 0 || u >= rows || x < 0 || x >= P) { printf("fold map out of row\n"); return 1; }
+                hits[u * P + x]++;
+            }
+        }
+    }
+    for (int i = 0; i < rows * P; ++i)
+        if (hits[i] != 1) { printf("fold map P%d element %d hit %d times\n", P, i, hits[i]); return 1; }
+    printf("fold map P%d: %d steps, %d pad elements\n", P, S, pads);
+    return pads == 2 * S * 16 - rows * P ? 0 : 1;
+}
+
 int main() {
     int bad = 0;
     for (int P : {14, 16}) bad |= check_rows(P);
@@ -89,6 +121,8 @@ int main() {
         for (int esz : {2, 4}) bad |= check(P, esz);
     for (int P : {14, 16}) bad |= check_tt(P);
     if (pe::tt_steps(14) != 37 || pe::tt_steps(16) != 48) { printf("tt step counts\n"); bad = 1; }
+    for (int P : {14, 16}) bad |= check_fold(P);
+    if (pe::fold_steps(14) != 19 || pe::fold_steps(16) != 24) { printf("fold step counts\n"); bad = 1; }
     if (pe::num_steps(14, 2) != 37 || pe::num_steps(16, 2) != 48) { printf("step counts\n"); bad = 1; }
     if (!bad) printf("OK\n");
     return bad;

@@ -34,6 +34,16 @@ def test_library_is_gfx950_code_object():
     assert b"gfx950" in data
 
 
+def test_config_struct_matches_header():
+    """The binding's pe_config has the header's fields, in order, all int32."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} pe_config;", src, flags=re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+)\s*;", body)
+    assert fields == [f for f, _ in pe.pe_config._fields_]
+    assert all(t is ctypes.c_int32 for _, t in pe.pe_config._fields_)
+    assert ctypes.sizeof(pe.pe_config) == 4 * len(fields)
+
+
 def test_num_rows_matches_page_shapes():
     assert pe.pe_num_rows([[1, 36, 54]]) == 1944          # mytransformer shape table
     assert pe.pe_num_rows([[1, 16, 64]]) == 1024          # Qwen2.5VL language-model page
@@ -62,6 +72,8 @@ def _cfg(**kw):
     (dict(out_dtype=-1), pe.PE_ERR_INVALID_ARG),
     (dict(out_order=5), pe.PE_ERR_INVALID_ARG),
     (dict(spatial_merge_size=0), pe.PE_ERR_INVALID_ARG),
+    (dict(image_fold=2), pe.PE_ERR_INVALID_ARG),
+    (dict(image_fold=1, weight_dtype=pe.PE_F32, out_dtype=pe.PE_F32), pe.PE_ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_config_before_touching_device(kw, code):
     h = ctypes.c_void_p(123)

@@ -36,7 +36,7 @@ class pe_config(ctypes.Structure):
     _fields_ = [("in_channels", ctypes.c_int32), ("temporal_patch_size", ctypes.c_int32),
                 ("patch_size", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
                 ("spatial_merge_size", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("out_order", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("out_order", ctypes.c_int32), ("image_fold", ctypes.c_int32)]
 
 
 def _load():
@@ -140,10 +140,12 @@ class PatchEmbed:
     weight  [E, 3, 2, P, P] bf16 or fp32 CUDA tensor (packed once at construction)
     bias    [E] same dtype, or None
     order   "merge" (2x2 merge-window rows) or "raster" (Conv3d view order) for frames input
+    image_fold  approximate mode for single-frame items: W[:, :, 0] + W[:, :, 1] folded into one
+            bf16 weight, half the matrix work (see pe.h); off by default
     """
 
     def __init__(self, weight, bias=None, *, order: str = "raster", out_dtype=None,
-                 spatial_merge_size: int = 2):
+                 spatial_merge_size: int = 2, image_fold: bool = False):
         import torch
         if weight.dim() != 5 or weight.shape[3] != weight.shape[4]:
             raise PEError(PE_ERR_INVALID_ARG, "weight must be [E, C, Tp, P, P]")
@@ -158,7 +160,7 @@ class PatchEmbed:
         self.order = order
         cfg = pe_config(int(C), int(Tp), int(P), int(E), int(spatial_merge_size),
                         _dtype_code(weight.dtype), _dtype_code(self.out_dtype),
-                        PE_ORDER_MERGE_WINDOW if order == "merge" else PE_ORDER_RASTER)
+                        PE_ORDER_MERGE_WINDOW if order == "merge" else PE_ORDER_RASTER, 1 if image_fold else 0)
         w = weight.contiguous()
         b = bias.contiguous() if bias is not None else None
         if b is not None and (b.dtype != weight.dtype or b.numel() != E):

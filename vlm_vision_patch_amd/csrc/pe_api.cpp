@@ -21,6 +21,7 @@ struct pe_handle_s {
     int steps;
     void *wpk;      // packed weight for frames, steps * packed_cols(E) * 64 bytes
     void *wpk_rows; // bf16: the same weight packed for patch rows (inside wpk's allocation); fp32: wpk
+    void *wpk_fold; // bf16 with image_fold: W[:, :, 0] + W[:, :, 1] in the fold map (inside wpk's allocation)
     float *bias32;  // fp32 bias or null
 };
 
@@ -106,6 +107,10 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     if (cfg->embed_dim <= 0 || cfg->embed_dim % 16 != 0 || cfg->embed_dim > 65536)
         return fail(PE_ERR_UNSUPPORTED, "embed_dim %d: must be a positive multiple of 16, at most 65536",
                     cfg->embed_dim);
+    if (cfg->image_fold != 0 && cfg->image_fold != 1)
+        return fail(PE_ERR_INVALID_ARG, "image_fold must be 0 or 1 (got %d)", cfg->image_fold);
+    if (cfg->image_fold && cfg->weight_dtype != PE_BF16)
+        return fail(PE_ERR_UNSUPPORTED, "image_fold needs a bf16 weight");
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -116,7 +121,9 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     const size_t frames_bytes = (size_t)steps * pe::packed_cols(cfg->embed_dim, wes) * 64;
     // bf16 keeps a second pack in the patch-rows order (fp32 uses one map for both inputs)
     const size_t rows_bytes = wes == 2 ? (size_t)pe::rows_steps(cfg->patch_size) * pe::packed_cols(cfg->embed_dim, wes) * 64 : 0;
-    const size_t wpk_bytes = frames_bytes + rows_bytes;
+    // and, with image_fold, a third in the folded map for single-frame items
+    const size_t fold_bytes = cfg->image_fold ? (size_t)pe::fold_steps(cfg->patch_size) * pe::packed_cols(cfg->embed_dim, wes) * 64 : 0;
+    const size_t wpk_bytes = frames_bytes + rows_bytes + fold_bytes;
 
     pe_handle h = new (std::nothrow) pe_handle_s;
     if (!h) return fail(PE_ERR_OOM, "host allocation failed");
@@ -130,6 +137,7 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     h->steps = steps;
     h->wpk = nullptr;
     h->wpk_rows = nullptr;
+    h->wpk_fold = nullptr;
     h->bias32 = nullptr;
     e = hipMalloc(&h->wpk, wpk_bytes);
     if (e != hipSuccess) {
@@ -138,6 +146,7 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
         return fail(PE_ERR_OOM, "hipMalloc(%zu) for the packed weight: %s", wpk_bytes, hipGetErrorString(e));
     }
     h->wpk_rows = rows_bytes ? static_cast<char *>(h->wpk) + frames_bytes : h->wpk;
+    h->wpk_fold = fold_bytes ? static_cast<char *>(h->wpk) + frames_bytes + rows_bytes : nullptr;
     if (bias) {
         e = hipMalloc(reinterpret_cast<void **>(&h->bias32), sizeof(float) * cfg->embed_dim);
         if (e != hipSuccess) {
@@ -147,9 +156,11 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
             return fail(PE_ERR_OOM, "hipMalloc for the bias: %s", hipGetErrorString(e));
         }
     }
-    e = pe::launch_pack(weight, wes, h->wpk, cfg->patch_size, cfg->embed_dim, false, st);
+    e = pe::launch_pack(weight, wes, h->wpk, cfg->patch_size, cfg->embed_dim, pe::kPackTT, st);
     if (e == hipSuccess && rows_bytes)
-        e = pe::launch_pack(weight, wes, h->wpk_rows, cfg->patch_size, cfg->embed_dim, true, st);
+        e = pe::launch_pack(weight, wes, h->wpk_rows, cfg->patch_size, cfg->embed_dim, pe::kPackRows, st);
+    if (e == hipSuccess && fold_bytes)
+        e = pe::launch_pack(weight, wes, h->wpk_fold, cfg->patch_size, cfg->embed_dim, pe::kPackFold, st);
     if (e == hipSuccess && bias) e = pe::launch_bias(bias, wes, h->bias32, cfg->embed_dim, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
@@ -281,8 +292,9 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
             ++i1;
         }
         a.kind = 1;
-        a.wpk = h->wpk;
         a.img = F[i0] == 1 ? 1 : 0;
+        a.fold = a.img && cfg.image_fold ? 1 : 0;
+        a.wpk = a.fold ? h->wpk_fold : h->wpk;
         a.mixg = mixed ? 1 : 0;
         a.rstr = (uint32_t)grid_thw[3 * i0 + 2] * (uint32_t)P;
         a.plane = (uint32_t)grid_thw[3 * i0 + 1] * (uint32_t)P * a.rstr;

@@ -37,6 +37,7 @@ struct FwdArgs {
     int32_t tiles_m, tiles_n;
     int32_t colmajor;      // tile order within an XCD's run: 1 = column tiles outermost
     int32_t img;           // 1: frames launch whose items are all single images (F = 1)
+    int32_t fold;          // 1: such a launch reads the folded weight (kAFold)
     int32_t mixg;          // 1: frames launch whose items differ in frame size (h, w)
     int32_t num_cus;       // compute units of the device (tile-size choice)
     uint32_t plane, rstr;  // channel and pixel-row strides (elements) when every item has one frame size
@@ -163,18 +164,37 @@ __host__ __device__ constexpr UFrag tt_frag(int P, int uf) {
 // weight (P = 14: the last lane group of step 36).
 __host__ __device__ constexpr int rows_steps(int P) { return (kC * kTp * P * P + 31) / 32; }
 
+// bf16 folded map for single-frame items (opt-in, approximate): both temporal slots of an image read
+// the same frame, so out = x . (W[:, :, 0] + W[:, :, 1]) over the C*P*P elements of one frame. The
+// folded weight is rounded to bf16 once. k-step s has four fragments g = 2j + h: lane half h of the
+// j-th 32x32x16 product reads fold pair p = 2s + j, half h. A pair is two unique fragments of the
+// same load kind (tt_frag's kinds), loaded by one instruction, or one fragment and a zero half:
+//   P % 8 == 0: p -> (2p, 2p + 1)                        (C*P*P/8 fragments, C*P*P/32 steps)
+//   P == 14:    p < 36 -> (2p, 2p + 1); p == 36 -> (72, none); p == 37 -> (73, none)   (19 steps)
+__host__ __device__ constexpr int fold_steps(int P) {
+    return P % 8 == 0 ? kC * P * (P / 8) / 4 : (P == 14 ? 19 : 0);
+}
+struct FoldPair { int uf0, uf1; };  // uf1 < 0: lanes 32-63 hold zeros
+__host__ __device__ constexpr FoldPair fold_pair(int P, int p) {
+    if (P % 8 != 0 && p >= 36) return FoldPair{36 + p, -1};
+    return FoldPair{2 * p, 2 * p + 1};
+}
+
 // k-steps of the packed weight: the temporal-split map for bf16, frag_piece's map for fp32
 __host__ __device__ constexpr int packed_steps(int P, int esz) {
     return esz == 2 ? tt_steps(P) : num_steps(P, esz);
 }
 
 // How the bf16 kernels read A: frames with two temporal slots, frames that are all single images
-// (both slots the same pixels), or pre-flattened patch rows (the rows map above).
-enum AMode { kAFrames = 0, kAImage = 1, kARows = 2 };
+// (both slots the same pixels), pre-flattened patch rows (the rows map above), or single images
+// against the folded weight (the fold map above).
+enum AMode { kAFrames = 0, kAImage = 1, kARows = 2, kAFold = 3 };
+// packed weight maps
+enum PackMap { kPackTT = 0, kPackRows = 1, kPackFold = 2 };
 
 // Launchers (pe_pack.hip and pe_fwd_p*.hip). Return the launch status.
-// rows_map: pack bf16 in the patch-rows order instead of the temporal-split order
-hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, bool rows_map, hipStream_t st);
+// map: PackMap (kPackRows and kPackFold are bf16 only)
+hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, int map, hipStream_t st);
 hipError_t launch_bias(const void *b, int b_esz, float *bias32, int E, hipStream_t st);
 hipError_t launch_forward(const FwdArgs &a, int P, int w_esz, int in_esz, int out_esz, hipStream_t st);
 // the forward kernels, one translation unit per patch size and input dtype (pe_fwd_p*.hip)

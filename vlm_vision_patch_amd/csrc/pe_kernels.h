@@ -111,7 +111,7 @@ __device__ __forceinline__ void store_chunk(void *out, const void *addend, int64
 // ----------------------------------------------------------------------------------------
 template <typename TW>
 __global__ void pe_pack_kernel(const TW *__restrict__ w, TW *__restrict__ wpk, int P, int E,
-                               int S, int rows_map) {
+                               int S, int map) {
     constexpr int esz = sizeof(TW);
     constexpr int epf = 16 / esz;
     constexpr int NB = pack_block(esz);
@@ -128,7 +128,38 @@ __global__ void pe_pack_kernel(const TW *__restrict__ w, TW *__restrict__ wpk, i
     const int s = (int)(t / ncb);
     const int e = cb * NB + n;
     TW vals[epf];
-    if (esz == 2 && rows_map) {
+    if constexpr (esz == 2) {
+        if (map == kPackFold) {
+            // folded map: fold pair p = 2s + j, half h of lane group g = 2j + h; each element is
+            // W[e, c, 0, py, px] + W[e, c, 1, py, px] (exact in fp32 for bf16 inputs within 2^16
+            // of each other in magnitude), rounded to bf16 once
+            const FoldPair fp = fold_pair(P, 2 * s + (g >> 1));
+            const int uf = (g & 1) ? fp.uf1 : fp.uf0;
+            uint16_t out[8];
+            const UFrag f = tt_frag(P, uf < 0 ? 0 : uf);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                int u = f.u1, x = f.x1 + j;
+                bool pad = e >= E || uf < 0;
+                if (f.kind == kUfSplit62 && j >= 6) { u = f.u2; x = f.x2 + (j - 6); }
+                if (f.kind == kUfTail4 && j >= 4) pad = true;
+                float v = 0.f;
+                if (!pad) {
+                    const int64_t i0 = ((((int64_t)e * kC + u / P) * kTp + 0) * P + u % P) * P + x;
+                    const int64_t i1 = i0 + (int64_t)P * P;
+                    const uint16_t b0 = reinterpret_cast<const uint16_t *>(w)[i0];
+                    const uint16_t b1 = reinterpret_cast<const uint16_t *>(w)[i1];
+                    v = __builtin_bit_cast(float, (uint32_t)b0 << 16) + __builtin_bit_cast(float, (uint32_t)b1 << 16);
+                }
+                out[j] = f32_to_bf16_rne(v);
+            }
+            uint16_t *dst = reinterpret_cast<uint16_t *>(wpk) + idx * 8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[j] = out[j];
+            return;
+        }
+    }
+    if (esz == 2 && map == kPackRows) {
         // patch-rows map: elements [32s + 8g, +8) of the flattened (c, t, py, px) filter
         const int K = kC * kTp * P * P;
 #pragma unroll
@@ -330,6 +361,12 @@ __device__ constexpr bool img_paired() {
 // per-step part of every address is one scalar for the whole launch; with items of different
 // frame sizes in one launch (MG true) each lane adds its own item's channel plane and pixel-row
 // stride (vpl, vrs) instead: two multiply-adds per fragment.
+// k-steps of a bf16 kernel for A mode AM
+template <int P, int AM>
+__host__ __device__ constexpr int a_steps() {
+    return AM == kARows ? rows_steps(P) : (AM == kAFold ? fold_steps(P) : tt_steps(P));
+}
+
 template <int P, int TM, int AM, int ISZ, int s, bool MG = false>
 __device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const uint32_t (&vb)[TM],
                                             uint32_t plane, uint32_t rstr, int h, AFrag<ISZ> (&dst)[TM][2],
@@ -355,6 +392,37 @@ __device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const u
                         if (h) zero_frag(dst[rb][j]);
                     }
                 }
+            }
+        });
+    } else if constexpr (AM == kAFold) {
+        // folded images: lane half h of sub-step j loads fragment fold_pair(2s + j) half h with
+        // one instruction (both halves have the same load kind); a pair without a second
+        // fragment loads the first twice and a_operands zeroes lanes 32-63
+        static_for<2>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr FoldPair fp = fold_pair(P, 2 * s + j);
+            constexpr bool two = fp.uf1 >= 0;
+            constexpr UFrag f0 = tt_frag(P, fp.uf0), f1 = tt_frag(P, two ? fp.uf1 : fp.uf0);
+            static_assert(f0.kind == f1.kind, "a fold pair is one load kind");
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb) {
+                uint32_t v1, v2 = 0u;
+                int so1 = 0, so2 = 0;
+                if constexpr (!MG) {
+                    so1 = (int)off(0, f0.u1, f0.x1);
+                    v1 = vb[rb] + ((two && h) ? off(0, f1.u1, f1.x1) - (uint32_t)so1 : 0u);
+                    if constexpr (f0.kind == kUfSplit62) {
+                        so2 = (int)off(0, f0.u2, f0.x2);
+                        v2 = vb[rb] + ((two && h) ? off(0, f1.u2, f1.x2) - (uint32_t)so2 : 0u);
+                    }
+                } else {
+                    v1 = vb[rb] + ((two && h) ? off(rb, f1.u1, f1.x1) : off(rb, f0.u1, f0.x1));
+                    if constexpr (f0.kind == kUfSplit62)
+                        v2 = vb[rb] + ((two && h) ? off(rb, f1.u2, f1.x2) : off(rb, f0.u2, f0.x2));
+                }
+                if constexpr (f0.kind == kUfFull) ld_whole<ISZ>(rsrc, v1, so1, dst[rb][j]);
+                else if constexpr (f0.kind == kUfSplit62) ld_split62<ISZ>(rsrc, v1, so1, v2, so2, dst[rb][j]);
+                else ld_tail4<ISZ>(rsrc, v1, so1, dst[rb][j]);
             }
         });
     } else if constexpr (AM == kAImage && img_paired<P, s>()) {
@@ -418,7 +486,7 @@ __device__ __forceinline__ void swap_halves(const u32x4 &x, u32x4 &lo, u32x4 &hi
     hi = u32x4{r0[1], r1[1], r2[1], r3[1]};
 }
 template <int P, int TM, int AM, int ISZ, int s>
-__device__ __forceinline__ void a_operands(const AFrag<ISZ> (&src)[TM][2], u32x4 (&dst)[TM][2]) {
+__device__ __forceinline__ void a_operands(const AFrag<ISZ> (&src)[TM][2], u32x4 (&dst)[TM][2], int h) {
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
         if constexpr (AM == kAImage && img_paired<P, s>()) {
@@ -426,6 +494,11 @@ __device__ __forceinline__ void a_operands(const AFrag<ISZ> (&src)[TM][2], u32x4
         } else {
             dst[rb][0] = frag_bf16<ISZ>(src[rb][0]);
             dst[rb][1] = frag_bf16<ISZ>(src[rb][1]);
+            if constexpr (AM == kAFold) {
+                // a fold pair without a second fragment: lanes 32-63 take zeros
+                if constexpr (fold_pair(P, 2 * s).uf1 < 0) dst[rb][0] = h ? u32x4{0u, 0u, 0u, 0u} : dst[rb][0];
+                if constexpr (fold_pair(P, 2 * s + 1).uf1 < 0) dst[rb][1] = h ? u32x4{0u, 0u, 0u, 0u} : dst[rb][1];
+            }
         }
     }
 }
@@ -661,7 +734,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     constexpr int NT = WM * WN * 64;
     constexpr int BM = WM * TM * 32;
     constexpr int BN = WN * TN * 32;
-    constexpr int S = AM == kARows ? rows_steps(P) : tt_steps(P);
+    constexpr int S = a_steps<P, AM>();
     constexpr int STAGE = BN * 64;                  // packed-weight bytes of one k-step
     constexpr int CH = (STAGE / 16 + NT - 1) / NT;  // 16-byte chunks per thread per k-step
     constexpr bool CH_EVEN = (STAGE / 16) % NT == 0;
@@ -821,7 +894,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         if constexpr (AST) read_a(s, ald_lds);
         const AFrag<ISZ>(&ald)[TM][2] = AST ? ald_lds : ald_regs;
         u32x4 af[TM][2];
-        a_operands<P, TM, AM, ISZ, s>(ald, af);
+        a_operands<P, TM, AM, ISZ, s>(ald, af, h);
         // fragment (j, cb) of this step: 1 KB at stage + (wn*TN + cb)*2 KB + j*1 KB
         const u32x4 *bs = reinterpret_cast<const u32x4 *>(lds + ((s / KS) & 1) * KBUF + (s % KS) * STAGE) +
                           wn * TN * 128 + lane;
@@ -987,7 +1060,7 @@ template <int P, int ISZ, int OSZ, int TM, int TN, int AD, int AM, bool MG>
 __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     constexpr int NW = 4;
     constexpr int BM = TM * 32, BN = TN * 32;
-    constexpr int S = AM == kARows ? rows_steps(P) : tt_steps(P);
+    constexpr int S = a_steps<P, AM>();
     constexpr int PITCH = BN + 8;                   // dwords per partial-tile row (8 mod 16)
     constexpr int PART = BM * PITCH * 4;            // bytes per wave's partial tile
     __shared__ __attribute__((aligned(16))) unsigned char lds[NW * PART];
@@ -1052,7 +1125,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     };
     auto mma = [&](auto sc, const Frags &d) {
         u32x4 af[TM][2];
-        a_operands<P, TM, AM, ISZ, decltype(sc)::value>(d.a, af);
+        a_operands<P, TM, AM, ISZ, decltype(sc)::value>(d.a, af, h);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1145,6 +1218,10 @@ inline hipError_t launch32(FwdArgs a, hipStream_t st) {
     const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
     if (a.kind == 0)
         hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kARows, false>), grid, block, 0, st, a);
+    else if (a.img && a.fold && a.mixg)
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAFold, true>), grid, block, 0, st, a);
+    else if (a.img && a.fold)
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAFold, false>), grid, block, 0, st, a);
     else if (a.img && a.mixg)
         hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAImage, true>), grid, block, 0, st, a);
     else if (a.img)
@@ -1164,6 +1241,10 @@ inline hipError_t launch_sk(FwdArgs a, hipStream_t st) {
     const dim3 grid(a.tiles_m * a.tiles_n), block(256);
     if (a.kind == 0)
         hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kARows, false>), grid, block, 0, st, a);
+    else if (a.img && a.fold && a.mixg)
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAFold, true>), grid, block, 0, st, a);
+    else if (a.img && a.fold)
+        hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAFold, false>), grid, block, 0, st, a);
     else if (a.img && a.mixg)
         hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kAImage, true>), grid, block, 0, st, a);
     else if (a.img)

@@ -4,17 +4,18 @@
 
 namespace pe {
 
-hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, bool rows_map, hipStream_t st) {
-    const int S = (w_esz == 2 && rows_map) ? rows_steps(P) : packed_steps(P, w_esz);
+hipError_t launch_pack(const void *w, int w_esz, void *wpk, int P, int E, int map, hipStream_t st) {
+    if (w_esz != 2 && map != kPackTT) return hipErrorInvalidValue;
+    const int S = map == kPackRows ? rows_steps(P) : (map == kPackFold ? fold_steps(P) : packed_steps(P, w_esz));
     const int64_t total = (int64_t)S * packed_cols(E, w_esz) * 4;
     const int threads = 256;
     const int blocks = (int)((total + threads - 1) / threads);
     if (w_esz == 2)
         hipLaunchKernelGGL(pe_pack_kernel<uint16_t>, dim3(blocks), dim3(threads), 0, st,
-                           static_cast<const uint16_t *>(w), static_cast<uint16_t *>(wpk), P, E, S, rows_map ? 1 : 0);
+                           static_cast<const uint16_t *>(w), static_cast<uint16_t *>(wpk), P, E, S, map);
     else
         hipLaunchKernelGGL(pe_pack_kernel<float>, dim3(blocks), dim3(threads), 0, st,
-                           static_cast<const float *>(w), static_cast<float *>(wpk), P, E, S, 0);
+                           static_cast<const float *>(w), static_cast<float *>(wpk), P, E, S, (int)kPackTT);
     return hipGetLastError();
 }
 
