@@ -164,10 +164,11 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
                 stats=stats, cold_ms=cold_ms)
 
 
-def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6):
+def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6, eager=False):
     """The PatchMerger front end on the workload's output rows: pe_layernorm over [N, E] in the
     output dtype (synthetic rows and parameters), alone and after the PatchEmbed as one step
-    (PatchEmbed, then the LayerNorm in place). Graph of K steps, median of `reps` replays."""
+    (PatchEmbed, then the LayerNorm in place). Graph of K steps, median of `reps` replays (eager:
+    K launches from Python between events, for counter runs)."""
     import torch
     import workloads
     import vlm_vision_patch_amd as pe
@@ -198,6 +199,19 @@ def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6):
 
     res = {}
     for name, fn in (("layernorm", ln_only), ("patch_embed_then_layernorm", pipeline)):
+        if eager:
+            with torch.cuda.stream(s):
+                for _ in range(warmup):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(s)
+                for _ in range(steps):
+                    fn()
+                e1.record(s)
+                torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / steps
+            continue
         with torch.cuda.stream(s):
             for _ in range(warmup):
                 fn()
@@ -230,6 +244,8 @@ def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6):
             "frac_hbm": round(ln_bytes / (ln_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
             "patch_embed_then_layernorm_ms": round(res["patch_embed_then_layernorm"], 5),
             "patch_embed_then_layernorm_patches_per_s": round(n / (res["patch_embed_then_layernorm"] / 1e3), 1),
+            "traffic": load_traffic("pe_layernorm_kernel", wl.name + "_layernorm"),
+            "timing": "K eager launches between HIP events" if eager else "graph of K steps, median of replays",
             "steps": steps}
 
 
@@ -377,7 +393,8 @@ def main():
     for spec in [v.strip() for v in args.extra.split(",") if v.strip()]:
         if spec.endswith("n"):
             e = int(spec[:-1])
-            also[workloads_name(e) + "_merger_layernorm"] = time_merger_front(e, max(5, min(args.steps, 50)))
+            also[workloads_name(e) + "_merger_layernorm"] = time_merger_front(e, max(5, min(args.steps, 50)),
+                                                                               eager=args.eager)
             continue
         as_rows = spec.endswith("r")
         with_add = spec.endswith("a")
