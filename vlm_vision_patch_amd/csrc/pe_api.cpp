@@ -305,6 +305,13 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
         a.n_rows = (int32_t)(row0[i1] - row0[i0]);
         a.n_items = i1 - i0;
         a.colmajor = (uint64_t)span * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
+        bool same = true;
+        for (int i = i0 + 1; i < i1 && same; ++i)
+            same = F[i] == F[i0] && grid_thw[3 * i] == grid_thw[3 * i0] && grid_thw[3 * i + 1] == grid_thw[3 * i0 + 1] &&
+                   grid_thw[3 * i + 2] == grid_thw[3 * i0 + 2];
+        a.uni = same ? 1 : 0;
+        a.u_rows = (int32_t)(row0[i0 + 1] - row0[i0]);
+        a.u_elems = (uint32_t)elems[i0];
         int64_t off = 0;
         for (int i = i0; i < i1; ++i) {
             pe::Item &it = a.items[i - i0];

@@ -41,6 +41,10 @@ struct FwdArgs {
     int32_t mixg;          // 1: frames launch whose items differ in frame size (h, w)
     int32_t num_cus;       // compute units of the device (tile-size choice)
     uint32_t plane, rstr;  // channel and pixel-row strides (elements) when every item has one frame size
+    // every item of the launch the same (t, h, w, F): item of a row by division, no table lookup
+    int32_t uni;
+    int32_t u_rows;        // rows per item (t*h*w)
+    uint32_t u_elems;      // input elements per item
     Item items[kMaxItems];
 };
 

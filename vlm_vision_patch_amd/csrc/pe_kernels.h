@@ -243,13 +243,24 @@ __device__ __forceinline__ PatchRef patch_of_row(const FwdArgs &a, int row) {
         pr.rstr = P;
         return pr;
     }
-    int lo = 0, hi = a.n_items - 1;
-    while (lo < hi) {  // last item whose first row <= row
-        const int mid = (lo + hi + 1) >> 1;
-        if (row >= a.items[mid].row0) lo = mid; else hi = mid - 1;
+    Item it;
+    uint32_t q;
+    if (a.uni) {
+        // identical items: the item index is a division, and every field but the offset is item 0's
+        // (scalar loads of the kernel arguments at fixed offsets, no dependent table reads)
+        const uint32_t idx = (uint32_t)row / (uint32_t)a.u_rows;
+        it = a.items[0];
+        it.x_off = idx * a.u_elems;
+        q = (uint32_t)row - idx * (uint32_t)a.u_rows;
+    } else {
+        int lo = 0, hi = a.n_items - 1;
+        while (lo < hi) {  // last item whose first row <= row
+            const int mid = (lo + hi + 1) >> 1;
+            if (row >= a.items[mid].row0) lo = mid; else hi = mid - 1;
+        }
+        it = a.items[lo];
+        q = (uint32_t)(row - it.row0);
     }
-    const Item it = a.items[lo];
-    const uint32_t q = (uint32_t)(row - it.row0);
     uint32_t tp, hp, wp;
     if (a.order == 0) {
         wp = q % (uint32_t)it.w;
@@ -783,15 +794,18 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     // read the two frames of the temporal patch: tstr = 0 for a repeated image frame), or for
     // patch rows the row plus 8 elements for lanes 32-63. The per-step part of each address is the
     // same for every row of the launch (one frame geometry per launch), so it is a scalar offset
-    // and the loads cost no vector arithmetic.
+    // and the loads cost no vector arithmetic. Computed once the first weight k-step's loads are in
+    // flight (they depend only on the tile's columns).
     uint32_t vb[TM], vpl[TM], vrs[TM];
+    auto rows_setup = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < TM; ++rb) {
-        const PatchRef p = patch_of_row<P>(a, row0 + (wm * TM + rb) * 32 + l32);
-        vb[rb] = AM == kARows ? (p.base + (h ? 8u : 0u)) * (uint32_t)ISZ : (p.base + (h ? p.tstr : 0u)) * (uint32_t)ISZ;
-        vpl[rb] = p.plane;
-        vrs[rb] = p.rstr;
-    }
+        for (int rb = 0; rb < TM; ++rb) {
+            const PatchRef p = patch_of_row<P>(a, row0 + (wm * TM + rb) * 32 + l32);
+            vb[rb] = AM == kARows ? (p.base + (h ? 8u : 0u)) * (uint32_t)ISZ : (p.base + (h ? p.tstr : 0u)) * (uint32_t)ISZ;
+            vpl[rb] = p.plane;
+            vrs[rb] = p.rstr;
+        }
+    };
 
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.in), (short)0, (int)a.in_bytes, kBufWord3);
@@ -952,6 +966,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 #pragma unroll
         for (int j = 0; j < (KS < S ? KS : S); ++j) {
             load_b(j, tmp);
+            if (j == 0 && !AST) rows_setup();
             store_b(j, tmp);
         }
     }
@@ -1081,14 +1096,18 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     const int h = lane >> 5, l32 = lane & 31;
     const int ncb = packed_cols(a.E, 2) >> 5;
 
+    // per lane and 32-row block: the patch's byte offset (item lookup); filled once this wave's
+    // first weight loads are in flight (they depend only on the tile's columns)
     uint32_t vb[TM], vpl[TM], vrs[TM];
+    auto rows_setup = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < TM; ++rb) {
-        const PatchRef p = patch_of_row<P>(a, row0 + rb * 32 + l32);
-        vb[rb] = AM == kARows ? (p.base + (h ? 8u : 0u)) * (uint32_t)ISZ : (p.base + (h ? p.tstr : 0u)) * (uint32_t)ISZ;
-        vpl[rb] = p.plane;
-        vrs[rb] = p.rstr;
-    }
+        for (int rb = 0; rb < TM; ++rb) {
+            const PatchRef p = patch_of_row<P>(a, row0 + rb * 32 + l32);
+            vb[rb] = AM == kARows ? (p.base + (h ? 8u : 0u)) * (uint32_t)ISZ : (p.base + (h ? p.tstr : 0u)) * (uint32_t)ISZ;
+            vpl[rb] = p.plane;
+            vrs[rb] = p.rstr;
+        }
+    };
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.in), (short)0, (int)a.in_bytes, kBufWord3);
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -1113,15 +1132,18 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     }
 
     struct Frags { AFrag<ISZ> a[TM][2]; u32x4 b[TN][2]; };
-    auto load = [&](auto sc, Frags &d) {
+    auto load_b = [&](auto sc, Frags &d) {
         constexpr int s = decltype(sc)::value;
-        load_a_step<P, TM, AM, ISZ, s, MG>(rsrc, vb, plane, rstr, h, d.a, vpl, vrs);
         static_for<2>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             const int sw = (int)(((uint32_t)s * (uint32_t)ncb * 2u + j) * 1024u);
 #pragma unroll
             for (int cb = 0; cb < TN; ++cb) d.b[cb][j] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)wb[cb], sw, 0);
         });
+    };
+    auto load = [&](auto sc, Frags &d) {
+        load_a_step<P, TM, AM, ISZ, decltype(sc)::value, MG>(rsrc, vb, plane, rstr, h, d.a, vpl, vrs);
+        load_b(sc, d);
     };
     auto mma = [&](auto sc, const Frags &d) {
         u32x4 af[TM][2];
@@ -1142,7 +1164,12 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
         Frags ring[AD + 1];
         static_for<(AD < n ? AD : n)>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            load(IC<lo + i>{}, ring[i]);
+            load_b(IC<lo + i>{}, ring[i]);
+        });
+        rows_setup();
+        static_for<(AD < n ? AD : n)>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            load_a_step<P, TM, AM, ISZ, lo + i, MG>(rsrc, vb, plane, rstr, h, ring[i].a, vpl, vrs);
         });
         static_for<n>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
