@@ -372,6 +372,42 @@ def test_forward_add(pe, case):
     check(got, ref, od, "add " + case)
 
 
+SPLIT_CASES = {
+    # name: (kind, items [(t, h, w, F)] or rows N, with an addend); more than two rounds of 256 x 256
+    # tiles with a last round under half full, rows checked around the last whole round's end
+    "patch_rows": ("patches", 28160, False),
+    "identical_images": ("frames", [(1, 64, 64, 1)] * 7, False),
+    "mixed_images_tail_mid_item": ("frames", [(1, 72, 72, 1)] * 4 + [(1, 48, 64, 1)] * 3, False),
+    "identical_images_add": ("frames", [(1, 64, 64, 1)] * 7, True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SPLIT_CASES))
+def test_partial_last_round(pe, case):
+    kind, items, with_add = SPLIT_CASES[case]
+    P, E = 14, 1280
+    K = 3 * 2 * P * P
+    w = make(1200, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(1201, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    if kind == "patches":
+        n = items
+        x = make(1202, (n, K), torch.bfloat16)
+        grid, frames, order = [[1, 1, n]], None, "raster"
+    else:
+        xs = [make(1203 + i, (F, 3, h * P, ww * P), torch.bfloat16) for i, (t, h, ww, F) in enumerate(items)]
+        x = torch.cat([a_.reshape(-1) for a_ in xs])
+        grid, frames, order = [[t, h, ww] for (t, h, ww, F) in items], [F for (*_, F) in items], "merge"
+        n = sum(t * h * ww for (t, h, ww) in grid)
+    # rows around the split (the first row of the last whole-round row tile .. the end) plus a sample
+    rt = (n + 255) // 256
+    main_rows = (rt * 5 // 256) * 256 // 5 * 256
+    near = set(range(max(0, main_rows - 300), min(n, main_rows + 300)))
+    rows = np.array(sorted(near | set(sampled_rows(n, 43, 400).tolist())), dtype=np.int64)
+    add = make(1210, (n, E), torch.bfloat16, "uniform", 0.5) if with_add else None
+    got, ref, od = run(pe, "split_" + case, x, w, b, grid, frames, kind=kind, order=order, rows=rows, add=add)
+    check(got, ref, od, "split " + case)
+
+
 def test_many_items_split_launches(pe):
     """More items than one launch's item table holds: the library splits the launches."""
     P, E = 14, 256
