@@ -1306,7 +1306,10 @@ __host__ inline int choose_tiles(int64_t n_rows, int E, int num_cus) {
 template <int P, int ESZ, int ISZ, int OSZ>
 inline hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
     if constexpr (ESZ == 4) {
-        // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps)
+        // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps); 32 x 160
+        // tiles where E allows (1024 x 1280 makes 256 of them: one round, where 32 x 128 tiles
+        // take 1.25; measured 38 us against 45-47 us), one weight k-step per LDS buffer
+        if (a.E % 160 == 0) return launch16<P, ESZ, OSZ, 1, 5, 2, 2, 1, 2, 2>(a, st);
         return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
     } else {
         // 8 waves of 32 x BN (two per SIMD), one weight k-step per LDS buffer (a barrier per k-step
