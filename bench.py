@@ -334,7 +334,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--extra", type=str, default="5,5r,5a,5n,5f,2f,5s8,4,6,1",
+    ap.add_argument("--extra", type=str, default="5,5r,5a,5n,5f,2f,5s8,3,4,6,1",
                     help="comma-separated further workloads reported under 'also' ('' for none); "
                          "a trailing r feeds that workload's patches as pre-flattened rows, a trailing "
                          "a fuses the add of an [N, E] tensor, a trailing n times the PatchMerger "
