@@ -11,24 +11,30 @@
 // registers that feed the matrix cores.
 //
 // K order. Any permutation of k applied to both A and W leaves the sum unchanged, so the
-// kernels use one that suits 16-byte fragments. A patch is C*Tp*P pixel rows of P elements,
-// r = (tt*C + c)*P + py. For bf16 and P = 14 each row gives one whole 8-element fragment
-// (px 0..7, one 16-byte load) and a 6-element rest; the rests of rows a, b, c, d form three
-// fragments (a[8:14] + d[8:10]), (b[8:14] + d[10:12]), (c[8:14] + d[12:14]), each a 12-byte
-// and a 4-byte load. 84 rows give 84 + 63 fragments; one zero fragment pads them to 37
-// k-steps of four fragments (1184 = 1176 + 8). For P = 16 every row is two whole fragments
-// (48 steps). fp32 uses 4-element fragments the same way (P = 14: 3 whole + pairs of
-// 2-element rests). The weight is packed once in exactly this order (pe_pack_kernel).
+// kernels use ones that suit 16-byte fragments (pe_internal.h holds the maps; the weight is
+// packed once in the same order by pe_pack_kernel):
+//  - bf16 frames, tt_frag: the two lane halves of a 32x32x16 product read the two temporal slots
+//    of the patch, each fragment one of the C*P pixel rows' 8-element pieces (P = 14: a whole
+//    px 0..7 piece, or a 6-element rest joined with 2 elements of a fourth row), 37 k-steps for
+//    P = 14 (1184 = 1176 + 8), 48 for P = 16;
+//  - bf16 patch rows, rows_steps: the stored (c, t, py, px) order, 32 contiguous elements a step;
+//  - bf16 single images with the opt-in fold, fold_pair: one frame's fragments against
+//    W[:, :, 0] + W[:, :, 1] (19 k-steps for P = 14);
+//  - fp32, frag_piece: 4-element fragments (P = 14: 3 whole + pairs of 2-element rests).
 //
 // bf16 kernel (pe_fwd32_kernel): v_mfma_f32_32x32x16_bf16, fp32 accumulate. (Measured on this
 // chip: the 32x32x16 form keeps the matrix pipe ~87% busy from a single wave per SIMD; the
 // 16x16x32 form reaches only ~54% from one wave.) A k-step of four fragments is two 32x32x16
 // products: lane l supplies row (or column) l % 32 and fragment g = 2j + l / 32 in sub-step j.
 // A workgroup computes a BM x BN tile with WM x WN waves, each wave TM x TN blocks of 32 x 32.
-// Each wave loads its own A fragments with raw buffer loads (32-bit offsets; reads past the
-// range return 0), so A never passes through LDS. The packed weight for one k-step and the
-// tile's columns is one contiguous run, staged in LDS (KS k-steps per buffer, two buffers) and
-// read as one conflict-free 1 KB ds_read_b128 per sub-step and 32-column block.
+// For frames each wave loads its own A fragments with raw buffer loads (32-bit offsets; reads
+// past the range return 0) straight into registers; patch rows are staged through LDS in whole
+// 128-byte pieces. The packed weight for one k-step and the tile's columns is one contiguous
+// run, staged in LDS (KS k-steps per buffer, two buffers) and read as one conflict-free 1 KB
+// ds_read_b128 per sub-step and 32-column block.
+//
+// bf16 split-k kernel (pe_fwd32_sk_kernel), for few rows: four waves share a 32 x 160 (or 128)
+// tile, each over a quarter of the k-steps, partial tiles summed through LDS.
 //
 // fp32 kernel (pe_fwd16_kernel): the same structure with 16x16 blocks and v_mfma_f32_16x16x4_f32.
 //
