@@ -1,5 +1,6 @@
-// pe_api.cpp -- the C ABI of include/pe.h: validation, the weight pre-pack at create, and the
-// launch plan of pe_forward (item tables, launch splitting). No allocation after pe_create.
+// pe_api.cpp -- the C ABI of include/pe.h: validation, the weight pre-pack at create, the
+// launch plan of pe_forward / pe_forward_add (item tables, launch splitting) and pe_layernorm's
+// checks. No allocation after pe_create.
 #include "pe.h"
 
 #include <math.h>
