@@ -164,6 +164,9 @@ CASES = [
     ("images_and_videos_one_size", 14, 640, [(1, 4, 6, 1), (2, 4, 6, 3), (1, 4, 6, 1), (1, 4, 6, 2),
                                              (1, 4, 6, 1)], "merge", torch.bfloat16, torch.bfloat16, True),
     ("t1_two_frames", 14, 320, [(1, 6, 4, 2)], "raster", torch.bfloat16, torch.bfloat16, False),
+    # wide embeddings: 32 column tiles of the split-k kernel, 16 of the large-tile kernel
+    ("e4096_splitk", 14, 4096, [(1, 20, 24, 1)], "merge", torch.bfloat16, torch.bfloat16, True),
+    ("e2304_p16_raster", 16, 2304, [(1, 12, 14, 1)], "raster", torch.bfloat16, torch.float32, True),
 ]
 
 
@@ -406,6 +409,18 @@ def test_partial_last_round(pe, case):
     add = make(1210, (n, E), torch.bfloat16, "uniform", 0.5) if with_add else None
     got, ref, od = run(pe, "split_" + case, x, w, b, grid, frames, kind=kind, order=order, rows=rows, add=add)
     check(got, ref, od, "split " + case)
+
+
+def test_wide_embedding_large_tiles(pe):
+    """E = 4096 over 8192 patches: 512 tiles of 256 x 256 (16 column tiles), sampled rows."""
+    P, E = 14, 4096
+    K = 3 * 2 * P * P
+    x = make(1300, (16, 3, 32 * P, 32 * P), torch.bfloat16)
+    w = make(1301, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(1302, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    rows = sampled_rows(8192, 47, 300)
+    got, ref, od = run(pe, "e4096_video", x, w, b, [[8, 32, 32]], [16], order="merge", rows=rows)
+    check(got, ref, od, "e4096 video")
 
 
 def test_many_items_split_launches(pe):
