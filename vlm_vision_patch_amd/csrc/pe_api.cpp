@@ -276,24 +276,29 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
         return PE_OK;
     }
 
-    // frames: launches of at most kMaxItems consecutive items, all single images or all not (the
-    // kernels load an image's shared temporal slots once), and at most kMaxLaunchBytes of input.
-    // Items of different frame sizes share a launch (the kernels then take each item's strides
-    // per lane instead of one scalar stride per launch).
+    // frames: launches of at most kMaxItems consecutive items and at most kMaxLaunchBytes of
+    // input. A launch whose items are all single images loads an image's shared temporal slots
+    // once; images mixed with videos run in the videos' launch (both temporal slots read the
+    // image's one frame, which is exact), since a launch per run of images or videos costs a
+    // launch and a partly idle last round each. With image_fold, single images are kept apart:
+    // only their launches use the folded weight. Items of different frame sizes share a launch
+    // (the kernels then take each item's strides per lane instead of one scalar stride).
+    const bool split_images = cfg.image_fold != 0;
     int64_t x0 = 0;  // element offset of item i0
     int i0 = 0;
     while (i0 < n_items) {
         int i1 = i0;
         int64_t span = 0;
-        bool mixed = false;
-        while (i1 < n_items && i1 - i0 < pe::kMaxItems && (F[i1] == 1) == (F[i0] == 1) &&
+        bool mixed = false, all_images = true;
+        while (i1 < n_items && i1 - i0 < pe::kMaxItems && (!split_images || (F[i1] == 1) == (F[i0] == 1)) &&
                (uint64_t)(span + elems[i1]) * ies <= kMaxLaunchBytes) {
             span += elems[i1];
             mixed = mixed || grid_thw[3 * i1 + 1] != grid_thw[3 * i0 + 1] || grid_thw[3 * i1 + 2] != grid_thw[3 * i0 + 2];
+            all_images = all_images && F[i1] == 1;
             ++i1;
         }
         a.kind = 1;
-        a.img = F[i0] == 1 ? 1 : 0;
+        a.img = all_images ? 1 : 0;
         a.fold = a.img && cfg.image_fold ? 1 : 0;
         a.wpk = a.fold ? h->wpk_fold : h->wpk;
         a.mixg = mixed ? 1 : 0;
