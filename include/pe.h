@@ -116,8 +116,9 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
  * Arithmetic: products of the input and weight values accumulated in fp32 together with the
  * fp32 bias, one round-to-nearest-even cast to the output dtype. Allocates nothing; does not
  * take ownership of input or out, which must stay valid until the stream work completes. One
- * kernel launch covers up to 64 consecutive items, images and videos alike (with image_fold,
- * runs of single images and of videos go to separate launches); their frame sizes may differ.
+ * kernel launch covers up to 64 consecutive items (any number of identical ones), images and
+ * videos alike (with image_fold, runs of single images and of videos go to separate launches);
+ * their frame sizes may differ.
  * Returns PE_OK, PE_ERR_INVALID_ARG, PE_ERR_SHAPE (a non-positive t/h/w, F_i inconsistent
  * with t_i, merge order with h or w not divisible by m, N >= 2^31), PE_ERR_UNSUPPORTED (bf16
  * input on an fp32 weight; one item's frames or one launch's patch rows beyond 4 GiB) or

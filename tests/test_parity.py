@@ -435,6 +435,28 @@ def test_many_items_split_launches(pe):
     check(got, ref, od, "150 items")
 
 
+IDENTICAL = {
+    # name: item list; identical items go to one launch whatever their number, the rest of a
+    # request keeps the 64-item table limit
+    "200_identical_images": [(1, 4, 6, 1)] * 200,
+    "70_identical_then_mixed": [(1, 4, 6, 1)] * 70 + [(1, 2, 4, 1), (2, 4, 2, 3)] + [(1, 4, 6, 1)] * 5,
+    "66_identical_videos": [(2, 2, 4, 4)] * 66,
+}
+
+
+@pytest.mark.parametrize("case", sorted(IDENTICAL))
+def test_identical_items_beyond_table(pe, case):
+    items = IDENTICAL[case]
+    P, E = 14, 320
+    xs = [make(1400 + i, (F, 3, h * P, w * P), torch.bfloat16) for i, (t, h, w, F) in enumerate(items)]
+    x = torch.cat([a.reshape(-1) for a in xs])
+    w = make(1401, (E, 3, 2, P, P), torch.bfloat16, "uniform", 0.03)
+    b = make(1402, (E,), torch.bfloat16, "uniform", 0.03)
+    grid = [[t, h, ww] for (t, h, ww, F) in items]
+    got, ref, od = run(pe, case, x, w, b, grid, [F for (*_, F) in items], order="merge")
+    check(got, ref, od, case)
+
+
 # ---------------------------------------------------------------------------------------------
 # integer inputs: exact results (the R1 == R2 check on the "Optimize VLM PatchEmbed" page)
 # ---------------------------------------------------------------------------------------------

@@ -276,8 +276,8 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
         return PE_OK;
     }
 
-    // frames: launches of at most kMaxItems consecutive items and at most kMaxLaunchBytes of
-    // input. A launch whose items are all single images loads an image's shared temporal slots
+    // frames: launches of at most kMaxItems consecutive items (any number when they are all
+    // alike) and at most kMaxLaunchBytes of input. A launch whose items are all single images loads an image's shared temporal slots
     // once; images mixed with videos run in the videos' launch (both temporal slots read the
     // image's one frame, which is exact), since a launch per run of images or videos costs a
     // launch and a partly idle last round each. With image_fold, single images are kept apart:
@@ -289,12 +289,21 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
     while (i0 < n_items) {
         int i1 = i0;
         int64_t span = 0;
-        bool mixed = false, all_images = true;
-        while (i1 < n_items && i1 - i0 < pe::kMaxItems && (!split_images || (F[i1] == 1) == (F[i0] == 1)) &&
+        bool mixed = false, all_images = true, same = true;
+        auto same_as_first = [&](int i) {
+            return F[i] == F[i0] && grid_thw[3 * i] == grid_thw[3 * i0] && grid_thw[3 * i + 1] == grid_thw[3 * i0 + 1] &&
+                   grid_thw[3 * i + 2] == grid_thw[3 * i0 + 2];
+        };
+        while (i1 < n_items && (!split_images || (F[i1] == 1) == (F[i0] == 1)) &&
                (uint64_t)(span + elems[i1]) * ies <= kMaxLaunchBytes) {
+            const bool still_same = same && same_as_first(i1);
+            // the item table holds kMaxItems entries; launches of identical items never read it
+            // past the first (a row's item is a division), so they may hold more
+            if (i1 - i0 >= pe::kMaxItems && !still_same) break;
             span += elems[i1];
             mixed = mixed || grid_thw[3 * i1 + 1] != grid_thw[3 * i0 + 1] || grid_thw[3 * i1 + 2] != grid_thw[3 * i0 + 2];
             all_images = all_images && F[i1] == 1;
+            same = still_same;
             ++i1;
         }
         a.kind = 1;
@@ -311,15 +320,11 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
         a.n_rows = (int32_t)(row0[i1] - row0[i0]);
         a.n_items = i1 - i0;
         a.colmajor = (uint64_t)span * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
-        bool same = true;
-        for (int i = i0 + 1; i < i1 && same; ++i)
-            same = F[i] == F[i0] && grid_thw[3 * i] == grid_thw[3 * i0] && grid_thw[3 * i + 1] == grid_thw[3 * i0 + 1] &&
-                   grid_thw[3 * i + 2] == grid_thw[3 * i0 + 2];
         a.uni = same ? 1 : 0;
         a.u_rows = (int32_t)(row0[i0 + 1] - row0[i0]);
         a.u_elems = (uint32_t)elems[i0];
         int64_t off = 0;
-        for (int i = i0; i < i1; ++i) {
+        for (int i = i0; i < i1 && i - i0 < pe::kMaxItems; ++i) {
             pe::Item &it = a.items[i - i0];
             it.row0 = (int32_t)(row0[i] - row0[i0]);
             it.t = grid_thw[3 * i];
