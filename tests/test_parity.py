@@ -458,6 +458,79 @@ def test_identical_items_beyond_table(pe, case):
 
 
 # ---------------------------------------------------------------------------------------------
+# inputs beyond one launch's buffer range (32-bit offsets): the library splits the launch. The big
+# input repeats a few seeded items with a period that does not divide the split point, so a wrong
+# input or output offset in a later launch yields another item's values. The oracle runs once per
+# distinct item on the sampled rows.
+# ---------------------------------------------------------------------------------------------
+
+LAUNCH_BYTES = 0xFFFFFFF0   # input bytes one launch addresses
+
+
+def test_frames_beyond_launch_range(pe):
+    P, E, hh, ww = 14, 1280, 72, 72
+    n_img, period = 720, 7
+    K = 3 * 2 * P * P
+    item_elems = 3 * hh * P * ww * P
+    per_launch = LAUNCH_BYTES // (item_elems * 2)           # 704 images of 1008 x 1008
+    assert per_launch < n_img and per_launch % period != 0
+    say("frames beyond the launch range: %d images of %dx%d, %.2f GB, split after %d" % (
+        n_img, hh * P, ww * P, n_img * item_elems * 2 / 1e9, per_launch))
+    imgs = [make(2600 + j, (1, 3, hh * P, ww * P), torch.bfloat16) for j in range(period)]
+    w = make(2610, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(2611, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    src = torch.stack([im.reshape(-1) for im in imgs]).to(DEV)
+    x = src[torch.arange(n_img, device=DEV) % period].reshape(-1)
+    del src
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV), order="merge")
+    out = mod(x, [[1, hh, ww]] * n_img, [1] * n_img)
+    torch.cuda.synchronize()
+    mod.close()
+    del x
+    R = hh * ww
+    rng = np.random.default_rng(2612)
+    items = sorted({0, 1, per_launch - 2, per_launch - 1, per_launch, per_launch + 1, n_img - 1}
+                   | set(rng.choice(n_img, 12, replace=False).tolist()))
+    local = np.array(sorted({0, 1, 255, 256, R - 2, R - 1} | set(rng.choice(R, 20, replace=False).tolist())),
+                     dtype=np.int64)
+    refs = {j: oracle.forward(imgs[j], w, b, grid=[[1, hh, ww]], frames=[1], order="merge", rows=local)
+            for j in sorted({i % period for i in items})}
+    rows = np.concatenate([i * R + local for i in items])
+    got = out[torch.as_tensor(rows, device=DEV)].double().cpu().numpy()
+    del out
+    torch.cuda.empty_cache()
+    ref = np.concatenate([refs[i % period] for i in items])
+    check(got, ref, torch.bfloat16, "frames beyond the launch range")
+
+
+def test_patch_rows_beyond_launch_range(pe):
+    P, E = 14, 1280
+    K = 3 * 2 * P * P
+    per_launch = LAUNCH_BYTES // (K * 2)                    # 1,826,091 rows of 2352 bytes
+    n, period = per_launch + 73_909, 4099
+    assert per_launch % period != 0
+    say("patch rows beyond the launch range: %d rows, %.2f GB, split after %d" % (n, n * K * 2 / 1e9, per_launch))
+    block = make(2620, (period, K), torch.bfloat16)
+    w = make(2621, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(2622, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    x = block.to(DEV)[torch.arange(n, device=DEV) % period]
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV))
+    out = mod(x, [[1, 1, n]], kind="patches")
+    torch.cuda.synchronize()
+    mod.close()
+    del x
+    rng = np.random.default_rng(2623)
+    rows = np.array(sorted({0, 1, per_launch - 2, per_launch - 1, per_launch, per_launch + 1, n - 2, n - 1}
+                           | set(rng.choice(n, 200, replace=False).tolist())), dtype=np.int64)
+    got = out[torch.as_tensor(rows, device=DEV)].double().cpu().numpy()
+    del out
+    torch.cuda.empty_cache()
+    sel = block[torch.as_tensor(rows % period)]
+    ref = oracle.forward(sel, w, b, grid=[[1, 1, len(rows)]], kind="patches")
+    check(got, ref, torch.bfloat16, "patch rows beyond the launch range")
+
+
+# ---------------------------------------------------------------------------------------------
 # integer inputs: exact results (the R1 == R2 check on the "Optimize VLM PatchEmbed" page)
 # ---------------------------------------------------------------------------------------------
 
