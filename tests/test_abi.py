@@ -55,6 +55,18 @@ def test_num_rows_matches_page_shapes():
     assert "non-positive" in pe.last_error()
 
 
+def test_num_rows_large_and_overflowing_grids():
+    big = 2 ** 31 - 1
+    assert pe.pe_num_rows([[big, big, 1]]) == big * big               # 4.6e18 still fits int64
+    assert pe.pe_num_rows([[big, 1, 1]] * 3) == 3 * big
+    assert pe.pe_num_rows([[big, big, 2]]) == 2 * big * big          # just below 2^63
+    for grid in ([[big, big, big]], [[big, big, 3]], [[big, big, 1]] * 3):
+        with pytest.raises(pe.PEError) as ei:
+            pe.pe_num_rows(grid)
+        assert ei.value.code == pe.PE_ERR_SHAPE
+        assert "overflows" in pe.last_error()
+
+
 def _cfg(**kw):
     c = dict(in_channels=3, temporal_patch_size=2, patch_size=14, embed_dim=1280, spatial_merge_size=2,
              weight_dtype=pe.PE_BF16, out_dtype=pe.PE_BF16, out_order=pe.PE_ORDER_MERGE_WINDOW)

@@ -598,6 +598,17 @@ def test_forward_error_paths(pe):
     # one item of frames beyond the 4 GiB launch range
     assert pe.lib.pe_forward(h, 1, X, 1, g(1, 2000, 2000), g(1), 1, O, None) == pe.PE_ERR_UNSUPPORTED
     assert "4 GiB" in pe.last_error()
+    # an item of 2^31 rows or more, also where t*h*w and its pixel count overflow 64 bits
+    big = 2 ** 31 - 1
+    for grid in ((1, 65536, 32768), (2 ** 30, big - 1, big - 1), (big, big, big)):
+        assert pe.lib.pe_forward(h, 1, X, 1, g(*grid), None, 1, O, None) == pe.PE_ERR_SHAPE, grid
+        assert "2^31 rows" in pe.last_error()
+        assert pe.lib.pe_forward(h, 0, X, 1, g(*grid), None, 1, O, None) == pe.PE_ERR_SHAPE, grid
+    # frames == NULL: a video of t = 2^30 temporal patches has 2^31 frames (counted in 64 bits)
+    mod_r = pe.PatchEmbed(w, order="raster")
+    assert pe.lib.pe_forward(mod_r._h, 1, X, 1, g(2 ** 30, 1, 1), None, 1, O, None) == pe.PE_ERR_UNSUPPORTED
+    assert "4 GiB" in pe.last_error()
+    mod_r.close()
     with pytest.raises(pe.PEError):
         mod(torch.zeros(10, dtype=torch.bfloat16, device=DEV), [[1, 2, 2]])   # wrong input size
     mod.close()

@@ -82,7 +82,10 @@ int64_t pe_num_rows(const int32_t *grid_thw, int32_t n_items) {
         const int32_t t = grid_thw[3 * i], h = grid_thw[3 * i + 1], w = grid_thw[3 * i + 2];
         if (t <= 0 || h <= 0 || w <= 0)
             return fail(PE_ERR_SHAPE, "item %d: grid (%d, %d, %d) has a non-positive entry", i, t, h, w);
-        n += (int64_t)t * h * w;
+        const int64_t th = (int64_t)t * h;  // < 2^62
+        if (th > (INT64_MAX - n) / w)
+            return fail(PE_ERR_SHAPE, "item %d: grid (%d, %d, %d): the row count overflows", i, t, h, w);
+        n += th * w;
     }
     return n;
 }
@@ -223,17 +226,21 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
         const int32_t t = grid_thw[3 * i], hh = grid_thw[3 * i + 1], ww = grid_thw[3 * i + 2];
         if (t <= 0 || hh <= 0 || ww <= 0)
             return fail(PE_ERR_SHAPE, "item %d: grid (%d, %d, %d) has a non-positive entry", i, t, hh, ww);
+        // an item's rows, like N, stay below 2^31; checked before the products below can overflow
+        if ((int64_t)t * hh >= ((int64_t)1 << 31) || (int64_t)t * hh * ww >= ((int64_t)1 << 31))
+            return fail(PE_ERR_SHAPE, "item %d: grid (%d, %d, %d) makes 2^31 rows or more", i, t, hh, ww);
         if (input_kind == PE_INPUT_FRAMES) {
-            const int32_t f = frames ? frames[i] : (t == 1 ? 1 : pe::kTp * t);
+            const int64_t f = frames ? (int64_t)frames[i] : (t == 1 ? 1 : (int64_t)pe::kTp * t);
             if (f <= 0 || (f + pe::kTp - 1) / pe::kTp != t)
-                return fail(PE_ERR_SHAPE, "item %d: %d frames do not make t = %d temporal patches", i, f, t);
+                return fail(PE_ERR_SHAPE, "item %d: %lld frames do not make t = %d temporal patches", i,
+                            (long long)f, t);
             if (merge && (hh % m || ww % m))
                 return fail(PE_ERR_SHAPE, "item %d: grid %d x %d not divisible by merge size %d", i, hh, ww, m);
-            F[i] = f;
-            elems[i] = (int64_t)f * pe::kC * hh * P * (int64_t)ww * P;
+            elems[i] = f * pe::kC * hh * P * (int64_t)ww * P;  // f <= 2t and t*hh*ww < 2^31: no overflow
             if ((uint64_t)elems[i] * ies > kMaxLaunchBytes)
                 return fail(PE_ERR_UNSUPPORTED, "item %d: %lld bytes of frames exceed the 4 GiB launch range",
                             i, (long long)(elems[i] * ies));
+            F[i] = (int32_t)f;  // < 2^31 after the byte check
         }
         row0[i] = N;
         N += (int64_t)t * hh * ww;
