@@ -119,10 +119,12 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
  * kernel launch covers up to 64 consecutive items (any number of identical ones), images and
  * videos alike (with image_fold, runs of single images and of videos go to separate launches);
  * their frame sizes may differ.
+ * Inputs beyond one launch's 4 GiB buffer range are split into several launches: frames at item
+ * boundaries, patch rows at any row.
  * Returns PE_OK, PE_ERR_INVALID_ARG, PE_ERR_SHAPE (a non-positive t/h/w, F_i inconsistent
  * with t_i, merge order with h or w not divisible by m, N >= 2^31), PE_ERR_UNSUPPORTED (bf16
- * input on an fp32 weight; one item's frames or one launch's patch rows beyond 4 GiB) or
- * PE_ERR_HIP (launch failure). Validation happens before any launch.
+ * input on an fp32 weight; one item's frames beyond 4 GiB) or PE_ERR_HIP (launch failure).
+ * Validation happens before any launch.
  */
 int pe_forward(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
                const int32_t *grid_thw, const int32_t *frames, int32_t n_items, void *out,
@@ -171,7 +173,8 @@ int pe_layernorm(const void *x, int32_t dtype, const void *gamma, const void *be
                  float eps, int64_t n_rows, int32_t dim, void *y, void *hip_stream);
 
 /* N = sum over items of t*h*w ("freechatgpt/mytransformer" section 3.2: N = t*h*w), or a
- * negative pe_status for a NULL grid, negative n_items or a non-positive entry. */
+ * negative pe_status: PE_ERR_INVALID_ARG for a NULL grid or negative n_items, PE_ERR_SHAPE for a
+ * non-positive entry or a sum beyond int64. */
 int64_t pe_num_rows(const int32_t *grid_thw, int32_t n_items);
 
 /* Release the handle and its device memory (synchronizes the device first). NULL -> PE_OK. */
