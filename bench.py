@@ -349,7 +349,8 @@ def main():
                     help="only run one plain device-to-device copy of BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus,
+        print("bench.py times one GPU only; --gpus %d is not supported (PatchEmbed rows are independent: "
+              "across GPUs the items are dealt out, one handle per device, with no exchange)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

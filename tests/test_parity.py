@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
 
-Tolerances (fixed by the workload statement, derived in the design doc):
+Tolerances (fixed for the workloads and checked against the arithmetic: bf16 products, fp32 accumulation):
   * fp32 output from fp32 inputs: max |err| <= 5e-4 (unit-variance inputs);
   * bf16 output: |err| <= 1e-3 + 1e-2 * |ref| elementwise;
   * fp32 output from bf16 inputs: max |err| <= 5e-4;
