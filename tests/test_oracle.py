@@ -366,6 +366,19 @@ def test_merge_order_within_window_reading():
     assert np.array_equal(raster_of_row, want.reshape(-1))
 
 
+@pytest.mark.parametrize("m,grid,F", [(1, (2, 3, 5), 4), (3, (1, 6, 9), 1), (3, (2, 3, 6), 3), (4, (2, 8, 4), 4)])
+def test_merge_order_any_window_size(m, grid, F):
+    """Window size m other than 2: the same windows-in-raster, row-major-inside reading, against
+    the raster grid reshaped to (t, h/m, m, w/m, m) and transposed; m = 1 is raster order itself."""
+    t, h, w = grid
+    pos = oracle.row_positions([list(grid)], [F], order="merge", m=m)
+    raster_of_row = (pos[:, 1] * h + pos[:, 2]) * w + pos[:, 3]
+    want = np.arange(t * h * w).reshape(t, h // m, m, w // m, m).transpose(0, 1, 3, 2, 4)
+    assert np.array_equal(raster_of_row, want.reshape(-1))
+    if m == 1:
+        assert np.array_equal(pos, oracle.row_positions([list(grid)], [F], order="raster"))
+
+
 # ---------------------------------------------------------------------------------------------
 # PatchMerger front end: LayerNorm over E, then the 2x2 concatenation ("freechatgpt/mytransformer"
 # section 3.2's vision encoder diagram and section 4.1's PatchMerger bullet)

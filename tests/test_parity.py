@@ -457,6 +457,37 @@ def test_identical_items_beyond_table(pe, case):
     check(got, ref, od, case)
 
 
+MERGE_SIZES = {
+    # window size m: items (t, h, w, F); h and w multiples of m
+    1: [(1, 3, 5, 1), (2, 2, 3, 4), (1, 7, 1, 1)],
+    3: [(1, 6, 9, 1), (2, 3, 6, 3), (1, 30, 21, 1)],
+    4: [(1, 8, 12, 1), (1, 4, 4, 1), (2, 4, 8, 4), (1, 32, 48, 1)],
+    "3_identical": [(1, 6, 6, 1)] * 5,
+}
+
+
+@pytest.mark.parametrize("case", sorted(MERGE_SIZES, key=str))
+def test_merge_window_sizes(pe, case):
+    """Merge-window order for window sizes other than 2 (the row map takes m at run time)."""
+    items = MERGE_SIZES[case]
+    m = case if isinstance(case, int) else int(case.split("_")[0])
+    P, E = 14, 320
+    K = 3 * 2 * P * P
+    xs = [make(2700 + i, (F, 3, h * P, w * P), torch.bfloat16) for i, (t, h, w, F) in enumerate(items)]
+    x = torch.cat([a.reshape(-1) for a in xs])
+    w = make(2701, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(2702, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    grid = [[t, h, ww] for (t, h, ww, F) in items]
+    frames = [F for (*_, F) in items]
+    say("merge window m=%d: items %s" % (m, items if len(items) <= 4 else "%d x %s" % (len(items), items[0])))
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV), order="merge", spatial_merge_size=m)
+    out = mod(x.to(DEV), grid, frames)
+    torch.cuda.synchronize()
+    mod.close()
+    ref = oracle.forward(x, w, b, grid=grid, frames=frames, order="merge", m=m)
+    check(out.double().cpu().numpy(), ref, torch.bfloat16, "merge m=%d" % m)
+
+
 # ---------------------------------------------------------------------------------------------
 # inputs beyond one launch's buffer range (32-bit offsets): the library splits the launch. The big
 # input repeats a few seeded items with a period that does not divide the split point, so a wrong
