@@ -167,6 +167,10 @@ CASES = [
     # wide embeddings: 32 column tiles of the split-k kernel, 16 of the large-tile kernel
     ("e4096_splitk", 14, 4096, [(1, 20, 24, 1)], "merge", torch.bfloat16, torch.bfloat16, True),
     ("e2304_p16_raster", 16, 2304, [(1, 12, 14, 1)], "raster", torch.bfloat16, torch.float32, True),
+    # fp32 weight and input, bf16 output (fp32 products, one cast)
+    ("f32_weight_bf16_out", 14, 640, [(1, 6, 8, 1), (2, 4, 2, 4)], "merge", torch.float32, torch.bfloat16, True),
+    ("f32_p16_bf16_out_e384", 16, 384, [(1, 4, 6, 1), (1, 10, 2, 1)], "raster", torch.float32, torch.bfloat16,
+     False),
 ]
 
 
@@ -189,6 +193,8 @@ def test_frames_edge_cases(pe, case):
                                        (16, 777, torch.bfloat16, torch.float32),
                                        (14, 300, torch.float32, torch.float32),
                                        (16, 65, torch.float32, torch.float32),
+                                       (14, 1024, torch.float32, torch.bfloat16),
+                                       (16, 300, torch.float32, torch.bfloat16),
                                        (14, 20000, torch.bfloat16, torch.bfloat16),
                                        (16, 9000, torch.bfloat16, torch.bfloat16)])
 def test_patch_rows(pe, P, N, dt, od):
