@@ -317,6 +317,57 @@ def test_concurrent_streams_one_handle(pe):
     mod.close()
 
 
+def test_host_threads_share_one_handle(pe):
+    """Several host threads call one handle at once, each on its own stream with its own request
+    (ctypes releases the GIL during the call). Every result equals the same call made alone, bit
+    for bit (the kernels are deterministic), and each thread reads back its own pe_last_error."""
+    import ctypes
+    import threading
+    P, E = 14, 640
+    K = 3 * 2 * P * P
+    w = make(2800, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(2801, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV), order="merge")
+    reqs = [([[1, 16, 64]], [1]), ([[1, 32, 32]] * 4, [1] * 4), ([[2, 8, 10]], [4]),
+            ([[1, 6, 8], [1, 10, 4], [3, 2, 2]], [1, 1, 6])]
+    say("host threads: %d requests on one handle" % len(reqs))
+    xs = [make(2810 + i, (mod.input_elements(g, f),), torch.bfloat16).to(DEV) for i, (g, f) in enumerate(reqs)]
+    alone = [mod(x, g, f) for x, (g, f) in zip(xs, reqs)]
+    torch.cuda.synchronize()
+    results = [[] for _ in reqs]
+    errs = [None] * len(reqs)
+
+    def worker(i):
+        g, f = reqs[i]
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            for k in range(16):
+                results[i].append(mod(xs[i], g, f))
+                if k == 8:
+                    # item i of i + 1 has an odd width: validation fails before any launch
+                    bad = (ctypes.c_int32 * (3 * (i + 1)))(*([1, 2, 2] * i + [1, 2, 3]))
+                    rc = pe.lib.pe_forward(mod._h, 1, 0x1000, 1, bad, None, i + 1, 0x2000, None)
+                    errs[i] = (rc, pe.last_error())
+        st.synchronize()
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(reqs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    mod.close()
+    for i in range(len(reqs)):
+        assert len(results[i]) == 16, "thread %d did not finish" % i
+        for o in results[i]:
+            assert torch.equal(o, alone[i]), "thread %d: result differs from the call made alone" % i
+        rc, msg = errs[i]
+        assert rc == pe.PE_ERR_SHAPE and ("item %d:" % i) in msg, (i, rc, msg)
+    # the results made alone are right
+    r0 = oracle.forward(xs[0].cpu(), w, b, grid=reqs[0][0], frames=reqs[0][1], order="merge")
+    check(alone[0].double().cpu().numpy(), r0, torch.bfloat16, "thread request 0")
+
+
 MIXED = {
     # name: (items [(t, h, w, F)], dtype, order); frame sizes differ within one launch
     "images_large": ([(1, 72, 72, 1), (1, 32, 48, 1), (1, 16, 64, 1), (1, 56, 40, 1), (1, 24, 24, 1),
