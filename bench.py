@@ -53,13 +53,17 @@ def algorithmic(wl, rows=False, add=False):
 
 def dominant_kernel(wl, num_cus=256):
     """Name of the kernel that does the step's work, by the library's tile choice for the largest
-    launch (a frames launch holds at most 64 items): in rounds of one workgroup per CU, 256 x 256
-    tiles cost ~30 us a round, 256 x 128 ~18 us and split-k ~8 us; the fewest (rounds x cost)
-    wins. fp32 runs the 16x16 kernel."""
+    launch (items that are all alike share one launch, others go 64 to a launch): in rounds of one
+    workgroup per CU, 256 x 256 tiles cost ~30 us a round, 256 x 128 ~18 us and split-k ~8 us; the
+    fewest (rounds x cost) wins. fp32 runs the 16x16 kernel."""
     if wl.w_dtype != "bf16":
         return "pe_fwd16_kernel"
     rows = [t * h * w for (t, h, w) in wl.grid]
-    n = max(sum(rows[i:i + 64]) for i in range(0, len(rows), 64))
+    frames = list(wl.frames) or [None] * len(rows)
+    if all(tuple(g) == tuple(wl.grid[0]) and f == frames[0] for g, f in zip(wl.grid, frames)):
+        n = sum(rows)
+    else:
+        n = max(sum(rows[i:i + 64]) for i in range(0, len(rows), 64))
     E = wl.embed
     rounds = lambda tiles: -(-tiles // num_cus)
     rt = -(-n // 256)
