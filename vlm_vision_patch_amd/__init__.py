@@ -168,16 +168,36 @@ class PatchEmbed:
         with torch.cuda.device(self.device):
             stream = torch.cuda.current_stream(self.device).cuda_stream
             self._h = pe_create(cfg, w.data_ptr(), b.data_ptr() if b is not None else None, stream)
+        self._plans = {}
+
+    _PLANS_MAX = 64
+
+    def _plan(self, grid_thw, frames, kind):
+        """(N, input elements, grid array, item count, frames array) of a request. The marshalled
+        arguments are kept per (kind, grid, frames) value, so a repeated request reuses them (the
+        library only reads the host arrays during the call)."""
+        g = grid_thw.tolist() if hasattr(grid_thw, "tolist") else grid_thw
+        f = frames.tolist() if (frames is not None and hasattr(frames, "tolist")) else frames
+        key = (kind, tuple(tuple(row) for row in g), None if f is None else tuple(f))
+        p = self._plans.get(key)
+        if p is None:
+            grid = [[int(v) for v in row] for row in g]
+            fr = None if f is None else [int(v) for v in f]
+            n = pe_num_rows(grid) if grid else 0
+            need = self.input_elements(grid, fr, kind) if n else 0
+            ga, ng = _i32_array(grid)
+            fa = _i32_array(fr)[0] if fr is not None else None
+            p = (n, need, ga, ng // 3, fa)
+            if len(self._plans) >= self._PLANS_MAX:
+                self._plans.clear()
+            self._plans[key] = p
+        return p
 
     def __call__(self, x, grid_thw, frames=None, *, kind: str = "frames", out=None, stream=None, add=None):
         """out = PatchEmbed(x) (+ add: an [N, E] tensor in the output dtype and row order, fused
         into the epilogue, e.g. the position embeddings that follow the PatchEmbed)."""
         import torch
-        grid = [[int(v) for v in row] for row in (grid_thw.tolist() if hasattr(grid_thw, "tolist") else grid_thw)]
-        fr = None
-        if frames is not None:
-            fr = [int(v) for v in (frames.tolist() if hasattr(frames, "tolist") else frames)]
-        n = pe_num_rows(grid) if grid else 0
+        n, need, ga, n_items, fa = self._plan(grid_thw, frames, kind)
         if out is None:
             out = torch.empty((n, self.embed_dim), dtype=self.out_dtype, device=self.device)
         elif tuple(out.shape) != (n, self.embed_dim) or out.dtype != self.out_dtype or not out.is_contiguous():
@@ -187,7 +207,6 @@ class PatchEmbed:
             return out
         if not x.is_cuda or x.device != self.device:
             raise PEError(PE_ERR_INVALID_ARG, "input must be on %s" % self.device)
-        need = self.input_elements(grid, fr, kind)
         if x.numel() != need:
             raise PEError(PE_ERR_SHAPE, "input has %d elements; the grid needs %d" % (x.numel(), need))
         x = x.contiguous()
@@ -195,14 +214,15 @@ class PatchEmbed:
             stream = torch.cuda.current_stream(self.device).cuda_stream
         ik = PE_INPUT_PATCHES if kind == "patches" else PE_INPUT_FRAMES
         if add is None:
-            pe_forward(self._h, ik, x.data_ptr(), _dtype_code(x.dtype), grid, fr, out.data_ptr(), stream)
+            _check(lib.pe_forward(self._h, ik, x.data_ptr(), _dtype_code(x.dtype), ga, fa, n_items,
+                                  out.data_ptr(), stream))
         else:
             if (tuple(add.shape) != (n, self.embed_dim) or add.dtype != self.out_dtype or not add.is_contiguous()
                     or add.device != self.device):
                 raise PEError(PE_ERR_INVALID_ARG, "add must be a contiguous [%d, %d] %s tensor on %s"
                               % (n, self.embed_dim, self.out_dtype, self.device))
-            pe_forward_add(self._h, ik, x.data_ptr(), _dtype_code(x.dtype), grid, fr, add.data_ptr(),
-                           out.data_ptr(), stream)
+            _check(lib.pe_forward_add(self._h, ik, x.data_ptr(), _dtype_code(x.dtype), ga, fa, n_items,
+                                      add.data_ptr(), out.data_ptr(), stream))
         return out
 
     def input_elements(self, grid, frames=None, kind="frames") -> int:
