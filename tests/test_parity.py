@@ -368,6 +368,35 @@ def test_host_threads_share_one_handle(pe):
     check(alone[0].double().cpu().numpy(), r0, torch.bfloat16, "thread request 0")
 
 
+def test_request_cache_of_the_binding(pe):
+    """PatchEmbed keeps the marshalled arguments of each request by value: more distinct requests
+    than it holds (it starts over when full), and a grid list changed in place between two calls,
+    still give the oracle's results."""
+    P, E = 14, 64
+    K = 3 * 2 * P * P
+    w = make(2900, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    mod = pe.PatchEmbed(w.to(DEV), order="merge")
+    say("binding request cache: %d distinct grids, then a grid changed in place" % (mod._PLANS_MAX + 6))
+    x = make(2901, (3 * 4 * P * 2 * (mod._PLANS_MAX + 6) * P,), torch.bfloat16)
+    xd = x.to(DEV)
+    for k in range(1, mod._PLANS_MAX + 7):
+        g = [[1, 4, 2 * k]]
+        n_el = 3 * 4 * P * 2 * k * P
+        out = mod(xd[:n_el], g, [1])
+        if k in (1, mod._PLANS_MAX, mod._PLANS_MAX + 1, mod._PLANS_MAX + 6):
+            ref = oracle.forward(x[:n_el], w, None, grid=g, frames=[1], order="merge")
+            check(out.double().cpu().numpy(), ref, torch.bfloat16, "grid %s" % g)
+    g = [[1, 4, 6]]
+    fr = [1]
+    o1 = mod(xd[:3 * 4 * P * 6 * P], g, fr)
+    g[0][2] = 8                               # same list object, new width
+    o2 = mod(xd[:3 * 4 * P * 8 * P], g, fr)
+    assert o2.shape[0] == 32 and o1.shape[0] == 24
+    ref = oracle.forward(x[:3 * 4 * P * 8 * P], w, None, grid=[[1, 4, 8]], frames=[1], order="merge")
+    check(o2.double().cpu().numpy(), ref, torch.bfloat16, "grid changed in place")
+    mod.close()
+
+
 MIXED = {
     # name: (items [(t, h, w, F)], dtype, order); frame sizes differ within one launch
     "images_large": ([(1, 72, 72, 1), (1, 32, 48, 1), (1, 16, 64, 1), (1, 56, 40, 1), (1, 24, 24, 1),
