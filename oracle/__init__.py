@@ -76,17 +76,48 @@ def _ptr(a, ct):
     return a.ctypes.data_as(ctypes.POINTER(ct)) if a is not None else None
 
 
+# Significant bits (implicit one included) and the exponent of the smallest normal number of
+# the two storage formats. Both have an 8-bit exponent field: bf16 is fp32 with 16 fewer
+# fraction bits.
+_FORMATS = {"bf16": (8, -126), "f32": (24, -126)}
+
+
 def round_to(a, dtype: str):
-    """Round values to ``dtype`` ("bf16" or "f32") with round-to-nearest-even (torch's cast),
-    returned as fp64. Used for the input cast to the weight dtype that the Qwen3-VL module
-    applies before its convolution ("Optimize VLM PatchEmbed", the forward of the
-    Qwen3VLVisionPatchEmbed class)."""
-    import torch
-    t = torch.as_tensor(_f64(a))
-    f32 = t.to(torch.float32)  # the inputs of this path are fp32 values: exact
-    if dtype == "f32":
-        return f32.to(torch.float64).numpy()
-    return f32.to(torch.bfloat16).to(torch.float64).numpy()
+    """Round each value ONCE to ``dtype`` ("bf16" or "f32"), round-to-nearest, ties to even,
+    and return the results as fp64 (exact: both formats are subsets of fp64).
+
+    This is the cast of the input to the weight dtype that the Qwen3-VL module applies before its
+    convolution ("Optimize VLM PatchEmbed", the forward of the Qwen3VLVisionPatchEmbed class),
+    written from the definition of the format rather than through another cast, so that an
+    fp64 value that is not an fp32 value is also rounded once:
+      - a finite nonzero v = f * 2^e with 0.5 <= |f| < 1 has, in a format with `bits` significant
+        bits and smallest normal exponent emin, the spacing q = 2^(max(e, emin + 1) - bits)
+        (below the normal range the spacing stays that of the subnormals);
+      - v / q is exact in fp64 (a power-of-two scaling), np.rint rounds it to the nearest integer
+        with ties to even, and multiplying back by q is exact;
+      - a result at or beyond 2^128 overflows to infinity with the sign of v;
+      - zeros (with their sign), infinities and NaN pass through.
+    """
+    if dtype not in _FORMATS:
+        raise ValueError("dtype must be 'bf16' or 'f32'")
+    bits, emin = _FORMATS[dtype]
+    v = _f64(a)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0)
+    x = v[fin]
+    _, e = np.frexp(x)
+    q = np.ldexp(1.0, np.maximum(e, emin + 1) - bits)
+    r = np.rint(x / q) * q
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, x), r)
+    out[fin] = r
+    return out
+
+
+def round_via_f32(a, dtype: str = "bf16"):
+    """fp64 -> fp32 -> dtype, each step rounded to nearest even: how a value the GPU holds in an
+    fp32 accumulator reaches its output dtype. Differs from ``round_to`` only where the first
+    rounding lands exactly on a midpoint of the second format (double rounding)."""
+    return round_to(round_to(a, "f32"), dtype)
 
 
 def num_rows(grid) -> int:

@@ -191,7 +191,7 @@ def test_merger_front_after_patch_embed(pe, out_dtype):
     got = merged.cpu().double().numpy()
     mod.close()
     pe_ref = oracle.forward(x, w, b, grid=grid, frames=frames, order="merge", m=2)
-    pe_ref = oracle.round_to(pe_ref, "bf16" if out_dtype == torch.bfloat16 else "f32")
+    pe_ref = oracle.round_via_f32(pe_ref, "bf16" if out_dtype == torch.bfloat16 else "f32")
     ref = oracle.merger_front(pe_ref, gam, bet, 1e-6, m=2)
     assert got.shape == ref.shape == (pe_ref.shape[0] // 4, 4 * E)
     mean = pe_ref.mean(axis=1, keepdims=True)

@@ -446,3 +446,73 @@ def test_merger_front_concatenates_2x2_neighbours():
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
     # the merged token count of the mytransformer shape table: [1944, 1280] rows -> 486 tokens
     assert oracle.merger_front(np.ones((1944, 8)) * np.arange(8), m=2).shape == (486, 32)
+
+
+# ---- the input cast: round to nearest, ties to even, applied once ("Optimize VLM PatchEmbed",
+# the Qwen3VLVisionPatchEmbed forward casts its input to the weight dtype). Expected values are
+# written out by hand from the formats: bf16 keeps 8 significant bits, so next to 1 its spacing
+# is 2^-7 and 1 + 2^-8 is the midpoint between 1 and 1 + 2^-7; fp32 keeps 24.
+
+def _r(v, dt):
+    return float(oracle.round_to(np.array([v]), dt)[0])
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_round_to_bf16_hand_values(sign):
+    s = sign
+    # ties go to the neighbour with an even last bit
+    assert _r(s * (1 + 2 ** -8), "bf16") == s * 1.0                      # 1 (even) vs 1 + 2^-7 (odd)
+    assert _r(s * (1 + 3 * 2 ** -8), "bf16") == s * (1 + 2 ** -6)        # 1 + 2^-7 (odd) vs 1 + 2^-6 (even)
+    assert _r(s * (2 + 2 ** -7), "bf16") == s * 2.0                      # midpoint one binade up
+    # off the midpoint by a little: the nearer neighbour, whatever its last bit
+    assert _r(s * (1 + 2 ** -8 + 2 ** -30), "bf16") == s * (1 + 2 ** -7)
+    assert _r(s * (1 + 2 ** -8 - 2 ** -30), "bf16") == s * 1.0
+    assert _r(s * (1 + 3 * 2 ** -8 - 2 ** -30), "bf16") == s * (1 + 2 ** -7)
+    # representable values stay
+    assert _r(s * (1 + 5 * 2 ** -7), "bf16") == s * (1 + 5 * 2 ** -7)
+    # a value given as fp32 rounds exactly once: 1 + 2^-8 + 2^-20 is an fp32 value above the midpoint
+    assert _r(np.float32(s * (1 + 2 ** -8 + 2 ** -20)), "bf16") == s * (1 + 2 ** -7)
+
+
+def test_round_to_bf16_is_one_rounding_not_two():
+    # through fp32 first, 1 + 2^-8 + 2^-30 would land on the bf16 midpoint 1 + 2^-8 and tie to 1
+    v = np.array([1 + 2 ** -8 + 2 ** -30, -(1 + 2 ** -8 + 2 ** -30)])
+    assert list(oracle.round_to(v, "bf16")) == [1 + 2 ** -7, -(1 + 2 ** -7)]
+    assert list(oracle.round_via_f32(v, "bf16")) == [1.0, -1.0]
+
+
+def test_round_to_bf16_range_edges():
+    big = (2 - 2 ** -7) * 2.0 ** 127                    # the largest finite bf16
+    assert _r(big, "bf16") == big
+    assert _r((2 - 2 ** -8 - 2 ** -20) * 2.0 ** 127, "bf16") == big   # below the midpoint to 2^128
+    assert _r((2 - 2 ** -8) * 2.0 ** 127, "bf16") == math.inf         # midpoint: even is 2^128, overflow
+    assert _r(-(2 - 2 ** -8) * 2.0 ** 127, "bf16") == -math.inf
+    # subnormals: spacing 2^-133 below 2^-126
+    assert _r(2.0 ** -133, "bf16") == 2.0 ** -133
+    assert _r(2.0 ** -134, "bf16") == 0.0                             # tie between 0 (even) and 2^-133
+    assert _r(3 * 2.0 ** -134, "bf16") == 2.0 ** -132                 # tie between 2^-133 (odd) and 2^-132
+    assert _r(1.5 * 2.0 ** -126 + 2.0 ** -134, "bf16") == 1.5 * 2.0 ** -126   # tie at the normal edge -> even
+    z = oracle.round_to(np.array([0.0, -0.0, np.inf, -np.inf, np.nan]), "bf16")
+    assert z[0] == 0.0 and not np.signbit(z[0]) and z[1] == 0.0 and np.signbit(z[1])
+    assert z[2] == np.inf and z[3] == -np.inf and np.isnan(z[4])
+
+
+def test_round_to_f32_hand_values():
+    assert _r(1 + 2 ** -24, "f32") == 1.0                             # tie, 1 is even
+    assert _r(1 + 3 * 2 ** -24, "f32") == 1 + 2 ** -22                # tie, 1 + 2^-22 is even
+    assert _r(1 + 2 ** -24 + 2 ** -40, "f32") == 1 + 2 ** -23
+    assert _r(-(1 + 2 ** -24 + 2 ** -40), "f32") == -(1 + 2 ** -23)
+    assert _r(2.0 ** -149, "f32") == 2.0 ** -149                      # smallest fp32 subnormal
+    assert _r(2.0 ** -150, "f32") == 0.0
+    assert _r((2 - 2 ** -24) * 2.0 ** 127, "f32") == math.inf
+
+
+def test_round_to_matches_torch_cast_on_fp32_values():
+    # special case that reduces to a library routine: for values that are already fp32, torch's
+    # fp32 -> bf16 cast (round to nearest even) must agree bit for bit
+    g = torch.Generator().manual_seed(5)
+    x = torch.cat([torch.randn(200000, generator=g) * s for s in (1e-38, 1e-3, 1.0, 1e3, 1e37)])
+    x = torch.cat([x, torch.tensor([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.0e38])])
+    want = x.to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_to(x, "bf16")
+    assert np.array_equal(got, want)
