@@ -147,6 +147,43 @@ int pe_forward_add(pe_handle h, int32_t input_kind, const void *input, int32_t i
                    const int32_t *grid_thw, const int32_t *frames, int32_t n_items, const void *addend,
                    void *out, void *hip_stream);
 
+/* How a launch reads its A operand (the patches). */
+typedef enum {
+    PE_A_FRAMES = 0,         /* frames with two temporal slots (videos, or images mixed with videos) */
+    PE_A_IMAGES = 1,         /* frames, every item one image frame (both slots the same pixels)    */
+    PE_A_PATCH_ROWS = 2,     /* pre-flattened patch rows                                            */
+    PE_A_FOLDED_IMAGES = 3   /* single images against the folded weight (image_fold = 1)            */
+} pe_a_mode;
+
+/* One kernel launch of a pe_forward call, as pe_forward_plan describes it. */
+typedef struct {
+    char kernel[32];      /* name of the HIP kernel the launch runs, e.g. "pe_fwd32_kernel"          */
+    int32_t tile_rows;    /* output rows x columns of one workgroup's tile                          */
+    int32_t tile_cols;
+    int64_t workgroups;   /* grid size                                                              */
+    int64_t row0;         /* first output row of the launch                                         */
+    int64_t n_rows;       /* output rows of the launch                                              */
+    int64_t in_offset;    /* byte offset of the launch's input within the input buffer              */
+    int64_t in_bytes;     /* bytes of input the launch may read                                     */
+    int32_t n_items;      /* items of a frames launch (0 for patch rows)                            */
+    int32_t a_mode;       /* pe_a_mode                                                              */
+} pe_launch_info;
+
+/*
+ * pe_forward_plan -- describe the kernel launches pe_forward (or pe_forward_add) would make for
+ *   this request, without launching anything and without touching device memory: the split into
+ *   launches, and per launch the kernel and tile chosen for it. Host-only; for profiling and for
+ *   callers that size their own timing around the launches.
+ *   h, input_kind, in_dtype, grid_thw, frames, n_items   as pe_forward (no device pointers needed).
+ *   info       host array of max_info entries (may be NULL when max_info is 0); the first
+ *              min(count, max_info) launches are written.
+ * Returns the number of launches (0 for n_items == 0), or a negative pe_status: the same request
+ * checks and codes as pe_forward, PE_ERR_INVALID_ARG for max_info < 0 or a NULL info with
+ * max_info > 0.
+ */
+int pe_forward_plan(pe_handle h, int32_t input_kind, int32_t in_dtype, const int32_t *grid_thw,
+                    const int32_t *frames, int32_t n_items, pe_launch_info *info, int32_t max_info);
+
 /*
  * pe_layernorm -- y[r, :] = (x[r, :] - mean_r) / sqrt(var_r + eps) * gamma + beta, for every row r
  *   of a row-major [n_rows, dim] tensor, asynchronously on hip_stream, on the current device.

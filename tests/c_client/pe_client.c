@@ -6,6 +6,10 @@
  *
  * usage: pe_client <dir>   (dir holds frames.bin, weight.bin, bias.bin, gamma.bin, beta.bin as
  *                           raw bf16, and meta.txt: P E t h w F; writes out.bin and ln.bin)
+ *        pe_client <dir> rows   (dir holds rows.bin: N pre-flattened patch rows [N, K] in
+ *                           in_dtype, weight.bin, bias.bin, and rows_meta.txt: P E N in_dtype;
+ *                           the rows go to a device buffer of exactly N*K elements, so the
+ *                           last row ends at the end of the allocation; writes rows_out.bin)
  */
 #include <hip/hip_runtime_api.h>
 #include <stdio.h>
@@ -54,8 +58,41 @@ static void *to_device(const void *h, size_t bytes) {
         }                                                                             \
     } while (0)
 
+static int run_rows(const char *dir) {
+    char path[1024];
+    snprintf(path, sizeof path, "%s/rows_meta.txt", dir);
+    FILE *m = fopen(path, "r");
+    int P, E, N, in_dtype;
+    if (!m || fscanf(m, "%d %d %d %d", &P, &E, &N, &in_dtype) != 4) { fprintf(stderr, "bad rows meta\n"); return 1; }
+    fclose(m);
+    size_t nx, nw, nb;
+    void *x = read_file(dir, "rows.bin", &nx), *wt = read_file(dir, "weight.bin", &nw);
+    void *b = read_file(dir, "bias.bin", &nb);
+    const size_t K = (size_t)3 * 2 * P * P, isz = in_dtype == PE_BF16 ? 2 : 4;
+    if (nx != (size_t)N * K * isz) { fprintf(stderr, "rows.bin holds %zu bytes, not N*K*%zu\n", nx, isz); return 1; }
+    void *dx = to_device(x, nx), *dw = to_device(wt, nw), *db = to_device(b, nb);   /* exactly N*K elements */
+    pe_config cfg = {3, 2, P, E, 2, PE_BF16, PE_BF16, PE_ORDER_RASTER, 0};
+    pe_handle hd = NULL;
+    CHECK(pe_create(&cfg, dw, db, NULL, &hd));
+    const int32_t grid[3] = {1, 1, N};
+    const size_t out_bytes = (size_t)N * (size_t)E * 2;
+    void *dout = NULL;
+    if (hipMalloc(&dout, out_bytes) != hipSuccess) return 3;
+    CHECK(pe_forward(hd, PE_INPUT_PATCHES, dx, in_dtype, grid, NULL, 1, dout, NULL));
+    if (hipDeviceSynchronize() != hipSuccess) return 3;
+    void *out = malloc(out_bytes);
+    if (hipMemcpy(out, dout, out_bytes, hipMemcpyDeviceToHost) != hipSuccess) return 3;
+    write_file(dir, "rows_out.bin", out, out_bytes);
+    CHECK(pe_destroy(hd));
+    hipFree(dx); hipFree(dw); hipFree(db); hipFree(dout);
+    free(x); free(wt); free(b); free(out);
+    printf("pe_client: %d patch rows x %d written\n", N, E);
+    return 0;
+}
+
 int main(int argc, char **argv) {
-    if (argc != 2) { fprintf(stderr, "usage: %s <dir>\n", argv[0]); return 1; }
+    if (argc == 3 && strcmp(argv[2], "rows") == 0) return run_rows(argv[1]);
+    if (argc != 2) { fprintf(stderr, "usage: %s <dir> [rows]\n", argv[0]); return 1; }
     const char *dir = argv[1];
     char path[1024];
     snprintf(path, sizeof path, "%s/meta.txt", dir);

@@ -113,9 +113,46 @@ static int check_fold(int P) {
     return pads == 2 * S * 16 - rows * P ? 0 : 1;
 }
 
+// Load placement of the patch-rows map: a load's bytes [start, start + len) must lie inside its own
+// row, for every lane half, sub-step and k-step, for bf16 (16-byte fragments) and fp32 input
+// (the same 8 elements, 32 bytes) -- in particular for the last row of a buffer, where any byte
+// past the row is past the caller's allocation. Every fragment that is not real must be one the
+// kernel zeroes (rows_frag_real false). The same for the 16-byte parts of the 128-byte pieces
+// that the large-tile kernel stages through LDS.
+static int check_rows_loads(int P) {
+    using namespace pe;
+    const int K = kC * kTp * P * P, S = rows_steps(P);
+    int relocated = 0;
+    for (int isz : {2, 4}) {
+        const int kb = K * isz;
+        for (int s = 0; s < S; ++s)
+            for (int j = 0; j < 2; ++j) {
+                if (!rows_frag_real(P, s, j, 0)) continue;   // not loaded at all
+                for (int h = 0; h < 2; ++h) {
+                    const int e0 = rows_load_elem(P, s, j, h);
+                    const int b0 = e0 * isz, b1 = b0 + 8 * isz;
+                    if (b0 < 0 || b1 > kb) { printf("rows load P%d isz%d s%d j%d h%d: bytes [%d, %d) leave a %d-byte row\n", P, isz, s, j, h, b0, b1, kb); return 1; }
+                    const bool real = rows_frag_real(P, s, j, h);
+                    if (real != (32 * s + 16 * j + 8 * h + 8 <= K)) { printf("rows fragment realness P%d\n", P); return 1; }
+                    if (!real) ++relocated;
+                }
+            }
+        const int nch = (kb + 127) / 128;
+        for (int c = 0; c < nch; ++c)
+            for (int q = 0; q < 8; ++q) {
+                const int b0 = c * 128 + 16 * piece_load_part(kb, c, q);
+                if (b0 < 0 || b0 + 16 > kb) { printf("piece load P%d isz%d c%d q%d: bytes [%d, %d) leave a %d-byte row\n", P, isz, c, q, b0, b0 + 16, kb); return 1; }
+                if (piece_part_real(kb, c, q) != (c * 128 + 16 * q + 16 <= kb)) { printf("piece realness P%d\n", P); return 1; }
+            }
+    }
+    printf("rows loads P%d: inside the row, %d fragments relocated\n", P, relocated);
+    return 0;
+}
+
 int main() {
     int bad = 0;
     for (int P : {14, 16}) bad |= check_rows(P);
+    for (int P : {14, 16}) bad |= check_rows_loads(P);
     if (pe::rows_steps(14) != 37 || pe::rows_steps(16) != 48) { printf("rows step counts\n"); bad = 1; }
     for (int P : {14, 16})
         for (int esz : {2, 4}) bad |= check(P, esz);

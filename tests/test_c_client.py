@@ -79,3 +79,35 @@ def test_c_client_matches_oracle(tmp_path):
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(pe_ref), 1e-30))) - 7)
     tol = 1e-3 + 1e-2 * np.abs(ln_ref) + np.abs(oracle._f64(gam)) * rstd * ulp
     assert np.all(np.abs(ln_got - ln_ref) <= tol)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,in_dtype", [(256, torch.bfloat16), (8192, torch.bfloat16), (1024, torch.float32)])
+def test_c_client_patch_rows_exact_buffer(tmp_path, n, in_dtype):
+    """Patch rows in a device buffer of exactly N*K elements (N chosen so that it ends on a 4 KiB
+    boundary): the loads of the last row's final fragment stay inside the row (the split-k kernel
+    at N = 256, the large-tile kernel that stages rows through LDS at N = 8192; fp32 rows rounded on
+    load), and the output matches the oracle."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("[case] C client patch rows: N=%d %s, P14, E1280, bias, exact-size buffer" % (n, in_dtype), flush=True)
+    P, E = 14, 1280
+    K = 3 * 2 * P * P
+    isz = 2 if in_dtype == torch.bfloat16 else 4
+    assert (n * K * isz) % 4096 == 0
+    x = workloads.random_tensor((n, K), seed=6100 + n, dtype=in_dtype)
+    wt = workloads.random_tensor((E, 3, 2, P, P), seed=6101, dtype=torch.bfloat16, dist="uniform", bound=1 / math.sqrt(K))
+    b = workloads.random_tensor((E,), seed=6102, dtype=torch.bfloat16, dist="uniform", bound=1 / math.sqrt(K))
+    d = str(tmp_path)
+    raw = bf16_bytes(x) if in_dtype == torch.bfloat16 else x.contiguous().numpy().tobytes()
+    open(os.path.join(d, "rows.bin"), "wb").write(raw)
+    open(os.path.join(d, "weight.bin"), "wb").write(bf16_bytes(wt))
+    open(os.path.join(d, "bias.bin"), "wb").write(bf16_bytes(b))
+    open(os.path.join(d, "rows_meta.txt"), "w").write("%d %d %d %d\n" % (P, E, n, 1 if in_dtype == torch.bfloat16 else 0))
+    exe = build_client(tmp_path)
+    r = subprocess.run([exe, d, "rows"], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr, flush=True)
+    assert r.returncode == 0
+    got = from_bf16_bytes(open(os.path.join(d, "rows_out.bin"), "rb").read(), (n, E))
+    ref = oracle.forward(x, wt, b, grid=[[1, 1, n]], kind="patches", cast_input_to="bf16")
+    assert np.all(np.abs(got - ref) <= 1e-3 + 1e-2 * np.abs(ref))

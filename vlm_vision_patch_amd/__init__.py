@@ -22,8 +22,9 @@ PE_ORDER_RASTER, PE_ORDER_MERGE_WINDOW = 0, 1
 PE_INPUT_PATCHES, PE_INPUT_FRAMES = 0, 1
 
 # every symbol include/pe.h declares
-EXPORTS = ("pe_create", "pe_forward", "pe_forward_add", "pe_layernorm", "pe_num_rows", "pe_destroy",
-           "pe_last_error")
+EXPORTS = ("pe_create", "pe_forward", "pe_forward_add", "pe_forward_plan", "pe_layernorm", "pe_num_rows",
+           "pe_destroy", "pe_last_error")
+PE_A_MODES = ("frames", "images", "patch_rows", "folded_images")
 
 
 class PEError(RuntimeError):
@@ -37,6 +38,13 @@ class pe_config(ctypes.Structure):
                 ("patch_size", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
                 ("spatial_merge_size", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("out_order", ctypes.c_int32), ("image_fold", ctypes.c_int32)]
+
+
+class pe_launch_info(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char * 32), ("tile_rows", ctypes.c_int32), ("tile_cols", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("row0", ctypes.c_int64), ("n_rows", ctypes.c_int64),
+                ("in_offset", ctypes.c_int64), ("in_bytes", ctypes.c_int64), ("n_items", ctypes.c_int32),
+                ("a_mode", ctypes.c_int32)]
 
 
 def _load():
@@ -55,6 +63,8 @@ def _load():
     lib.pe_forward.argtypes = [vp, i32, vp, i32, pi32, pi32, i32, vp, vp]
     lib.pe_forward_add.restype = ctypes.c_int
     lib.pe_forward_add.argtypes = [vp, i32, vp, i32, pi32, pi32, i32, vp, vp, vp]
+    lib.pe_forward_plan.restype = ctypes.c_int
+    lib.pe_forward_plan.argtypes = [vp, i32, i32, pi32, pi32, i32, ctypes.POINTER(pe_launch_info), i32]
     lib.pe_layernorm.restype = ctypes.c_int
     lib.pe_layernorm.argtypes = [vp, i32, vp, vp, i32, ctypes.c_float, i64, i32, vp, vp]
     lib.pe_num_rows.restype = i64
@@ -106,6 +116,21 @@ def pe_forward_add(handle: int, input_kind: int, input_ptr: int, in_dtype: int, 
     _check(lib.pe_forward_add(handle, input_kind, input_ptr, in_dtype, g, f, n // 3, addend_ptr, out_ptr, stream))
 
 
+def pe_forward_plan(handle: int, input_kind: int, in_dtype: int, grid_thw, frames) -> list:
+    """The launches pe_forward would make for this request, as dicts (kernel name, tile, grid,
+    rows, input range, items, A mode)."""
+    g, n = _i32_array(grid_thw)
+    f = _i32_array(frames)[0] if frames is not None else None
+    count = lib.pe_forward_plan(handle, input_kind, in_dtype, g, f, n // 3, None, 0)
+    if count < 0:
+        raise PEError(count, last_error())
+    info = (pe_launch_info * max(1, count))()
+    _check(min(0, lib.pe_forward_plan(handle, input_kind, in_dtype, g, f, n // 3, info, count)))
+    return [{"kernel": i.kernel.decode(), "tile": [i.tile_rows, i.tile_cols], "workgroups": i.workgroups,
+             "row0": i.row0, "n_rows": i.n_rows, "in_offset": i.in_offset, "in_bytes": i.in_bytes,
+             "n_items": i.n_items, "a_mode": PE_A_MODES[i.a_mode]} for i in info[:count]]
+
+
 def pe_layernorm(x_ptr: int, dtype: int, gamma_ptr: int | None, beta_ptr: int | None, param_dtype: int,
                  eps: float, n_rows: int, dim: int, y_ptr: int, stream: int | None) -> None:
     _check(lib.pe_layernorm(x_ptr, dtype, gamma_ptr, beta_ptr, param_dtype, eps, n_rows, dim, y_ptr, stream))
@@ -132,6 +157,20 @@ def _dtype_code(dt):
     if dt == torch.float32:
         return PE_F32
     raise PEError(PE_ERR_UNSUPPORTED, "dtype %s: only bfloat16 and float32" % dt)
+
+
+def _keep_for_stream(tensors, stream, device):
+    """Tensors this binding allocated (an output, a contiguous copy of the input) are freed by
+    torch's caching allocator on the stream current at allocation. When the kernel runs on another
+    stream, mark them as used there, so their memory is not handed out again before that stream's
+    work is done."""
+    import torch
+    if stream is None or stream == torch.cuda.current_stream(device).cuda_stream:
+        return
+    ext = torch.cuda.ExternalStream(stream, device=device)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(ext)
 
 
 class PatchEmbed:
@@ -198,8 +237,10 @@ class PatchEmbed:
         into the epilogue, e.g. the position embeddings that follow the PatchEmbed)."""
         import torch
         n, need, ga, n_items, fa = self._plan(grid_thw, frames, kind)
+        made = []   # tensors allocated here (see _keep_for_stream)
         if out is None:
             out = torch.empty((n, self.embed_dim), dtype=self.out_dtype, device=self.device)
+            made.append(out)
         elif tuple(out.shape) != (n, self.embed_dim) or out.dtype != self.out_dtype or not out.is_contiguous():
             raise PEError(PE_ERR_INVALID_ARG, "out must be a contiguous [%d, %d] %s tensor"
                           % (n, self.embed_dim, self.out_dtype))
@@ -209,9 +250,14 @@ class PatchEmbed:
             raise PEError(PE_ERR_INVALID_ARG, "input must be on %s" % self.device)
         if x.numel() != need:
             raise PEError(PE_ERR_SHAPE, "input has %d elements; the grid needs %d" % (x.numel(), need))
-        x = x.contiguous()
+        xc = x.contiguous()
+        if xc.data_ptr() != x.data_ptr():
+            made.append(xc)
+        x = xc
         if stream is None:
             stream = torch.cuda.current_stream(self.device).cuda_stream
+        else:
+            _keep_for_stream(made, stream, self.device)
         ik = PE_INPUT_PATCHES if kind == "patches" else PE_INPUT_FRAMES
         if add is None:
             _check(lib.pe_forward(self._h, ik, x.data_ptr(), _dtype_code(x.dtype), ga, fa, n_items,
@@ -224,6 +270,14 @@ class PatchEmbed:
             _check(lib.pe_forward_add(self._h, ik, x.data_ptr(), _dtype_code(x.dtype), ga, fa, n_items,
                                       add.data_ptr(), out.data_ptr(), stream))
         return out
+
+    def plan(self, grid_thw, frames=None, *, kind: str = "frames", in_dtype=None) -> list:
+        """The kernel launches a call with this grid makes (pe_forward_plan): kernel name, tile,
+        workgroups, rows and input range per launch. Nothing is launched."""
+        ik = PE_INPUT_PATCHES if kind == "patches" else PE_INPUT_FRAMES
+        g = grid_thw.tolist() if hasattr(grid_thw, "tolist") else grid_thw
+        return pe_forward_plan(self._h, ik, _dtype_code(in_dtype if in_dtype is not None else self.weight_dtype),
+                               g, frames)
 
     def input_elements(self, grid, frames=None, kind="frames") -> int:
         """Elements the library will read for this grid (the C ABI trusts the caller on this)."""
@@ -265,12 +319,16 @@ def layer_norm(x, gamma=None, beta=None, eps: float = 1e-6, *, out=None, stream=
                 raise PEError(PE_ERR_INVALID_ARG, "gamma / beta must be contiguous [%d] tensors of one dtype "
                               "on %s" % (dim, x.device))
             pdt = p.dtype
+    made = []
     if out is None:
         out = torch.empty_like(x)
+        made.append(out)
     elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
         raise PEError(PE_ERR_INVALID_ARG, "out must be a contiguous tensor like x")
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
+    else:
+        _keep_for_stream(made, stream, x.device)
     with torch.cuda.device(x.device):
         pe_layernorm(x.data_ptr(), _dtype_code(x.dtype), gamma.data_ptr() if gamma is not None else None,
                      beta.data_ptr() if beta is not None else None,

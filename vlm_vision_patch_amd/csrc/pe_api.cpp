@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "pe_internal.h"
+#include "pe_plan.h"
 
 struct pe_handle_s {
     pe_config cfg;
@@ -64,8 +65,6 @@ struct DeviceGuard {
         if (switched) (void)hipSetDevice(prev);
     }
 };
-
-constexpr uint64_t kMaxLaunchBytes = 0xFFFFFFF0ull;  // buffer range of one launch (32-bit offsets)
 
 }  // namespace
 
@@ -194,6 +193,41 @@ int pe_destroy(pe_handle h) {
 
 namespace {
 
+void fill_request(pe_handle h, int32_t input_kind, int32_t in_dtype, const int32_t *grid_thw, const int32_t *frames,
+                  int32_t n_items, pe::PlanRequest &rq) {
+    const pe_config &cfg = h->cfg;
+    rq.P = cfg.patch_size;
+    rq.E = cfg.embed_dim;
+    rq.m = cfg.spatial_merge_size;
+    rq.weight_esz = esize(cfg.weight_dtype);
+    rq.in_esz = esize(in_dtype);
+    rq.out_esz = esize(cfg.out_dtype);
+    rq.merge = cfg.out_order == PE_ORDER_MERGE_WINDOW;
+    rq.image_fold = cfg.image_fold;
+    rq.num_cus = h->num_cus;
+    rq.input_kind = input_kind;
+    rq.grid_thw = grid_thw;
+    rq.frames = frames;
+    rq.n_items = n_items;
+}
+
+// checks of pe_forward's handle and dtype arguments (the plan checks the grid)
+int check_request(pe_handle h, int32_t input_kind, int32_t in_dtype, int32_t n_items, const int32_t *grid_thw) {
+    if (!h) return fail(PE_ERR_INVALID_ARG, "handle is NULL");
+    if (n_items < 0) return fail(PE_ERR_INVALID_ARG, "n_items must be >= 0 (got %d)", n_items);
+    if (n_items == 0) return PE_OK;
+    if (!grid_thw) return fail(PE_ERR_INVALID_ARG, "grid_thw is NULL");
+    if (input_kind != PE_INPUT_PATCHES && input_kind != PE_INPUT_FRAMES)
+        return fail(PE_ERR_INVALID_ARG, "bad input_kind %d", input_kind);
+    if (!dtype_ok(in_dtype)) return fail(PE_ERR_INVALID_ARG, "bad in_dtype %d", in_dtype);
+    const pe_config &cfg = h->cfg;
+    // bf16 weight: bf16 input, or fp32 input rounded to bf16 on load; fp32 weight: fp32 input
+    if (in_dtype != cfg.weight_dtype && !(cfg.weight_dtype == PE_BF16 && in_dtype == PE_F32))
+        return fail(PE_ERR_UNSUPPORTED, "in_dtype %d with weight dtype %d: supported are bf16/bf16, "
+                    "fp32/bf16 (rounded on load) and fp32/fp32", in_dtype, cfg.weight_dtype);
+    return PE_OK;
+}
+
 // pe_forward and pe_forward_add: addend is null for the plain forward
 int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_dtype,
                  const int32_t *grid_thw, const int32_t *frames, int32_t n_items, const void *addend,
@@ -204,147 +238,30 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
     if (!grid_thw) return fail(PE_ERR_INVALID_ARG, "grid_thw is NULL");
     if (!input) return fail(PE_ERR_INVALID_ARG, "input is NULL");
     if (!out) return fail(PE_ERR_INVALID_ARG, "out is NULL");
-    if (input_kind != PE_INPUT_PATCHES && input_kind != PE_INPUT_FRAMES)
-        return fail(PE_ERR_INVALID_ARG, "bad input_kind %d", input_kind);
-    if (!dtype_ok(in_dtype)) return fail(PE_ERR_INVALID_ARG, "bad in_dtype %d", in_dtype);
+    const int crc = check_request(h, input_kind, in_dtype, n_items, grid_thw);
+    if (crc != PE_OK) return crc;
     const pe_config &cfg = h->cfg;
-    // bf16 weight: bf16 input, or fp32 input rounded to bf16 on load; fp32 weight: fp32 input
-    if (in_dtype != cfg.weight_dtype && !(cfg.weight_dtype == PE_BF16 && in_dtype == PE_F32))
-        return fail(PE_ERR_UNSUPPORTED, "in_dtype %d with weight dtype %d: supported are bf16/bf16, "
-                    "fp32/bf16 (rounded on load) and fp32/fp32", in_dtype, cfg.weight_dtype);
 
-    const int P = cfg.patch_size, E = cfg.embed_dim, m = cfg.spatial_merge_size;
-    const int ies = esize(in_dtype), oes = esize(cfg.out_dtype), wes = esize(cfg.weight_dtype);
-    const int64_t K = (int64_t)pe::kC * pe::kTp * P * P;
-    const bool merge = input_kind == PE_INPUT_FRAMES && cfg.out_order == PE_ORDER_MERGE_WINDOW;
-
-    // ---- validate every item before any launch
-    std::vector<int32_t> F(n_items);
-    std::vector<int64_t> row0(n_items + 1), elems(n_items);
-    int64_t N = 0;
-    for (int i = 0; i < n_items; ++i) {
-        const int32_t t = grid_thw[3 * i], hh = grid_thw[3 * i + 1], ww = grid_thw[3 * i + 2];
-        if (t <= 0 || hh <= 0 || ww <= 0)
-            return fail(PE_ERR_SHAPE, "item %d: grid (%d, %d, %d) has a non-positive entry", i, t, hh, ww);
-        // an item's rows, like N, stay below 2^31; checked before the products below can overflow
-        if ((int64_t)t * hh >= ((int64_t)1 << 31) || (int64_t)t * hh * ww >= ((int64_t)1 << 31))
-            return fail(PE_ERR_SHAPE, "item %d: grid (%d, %d, %d) makes 2^31 rows or more", i, t, hh, ww);
-        if (input_kind == PE_INPUT_FRAMES) {
-            const int64_t f = frames ? (int64_t)frames[i] : (t == 1 ? 1 : (int64_t)pe::kTp * t);
-            if (f <= 0 || (f + pe::kTp - 1) / pe::kTp != t)
-                return fail(PE_ERR_SHAPE, "item %d: %lld frames do not make t = %d temporal patches", i,
-                            (long long)f, t);
-            if (merge && (hh % m || ww % m))
-                return fail(PE_ERR_SHAPE, "item %d: grid %d x %d not divisible by merge size %d", i, hh, ww, m);
-            elems[i] = f * pe::kC * hh * P * (int64_t)ww * P;  // f <= 2t and t*hh*ww < 2^31: no overflow
-            if ((uint64_t)elems[i] * ies > kMaxLaunchBytes)
-                return fail(PE_ERR_UNSUPPORTED, "item %d: %lld bytes of frames exceed the 4 GiB launch range",
-                            i, (long long)(elems[i] * ies));
-            F[i] = (int32_t)f;  // < 2^31 after the byte check
-        }
-        row0[i] = N;
-        N += (int64_t)t * hh * ww;
-    }
-    row0[n_items] = N;
-    if (N >= ((int64_t)1 << 31)) return fail(PE_ERR_SHAPE, "N = %lld rows: must be < 2^31", (long long)N);
+    pe::PlanRequest rq;
+    fill_request(h, input_kind, in_dtype, grid_thw, frames, n_items, rq);
+    std::vector<pe::Launch> plan;
+    std::string err;
+    const int rc = pe::plan_forward(rq, plan, err);
+    if (rc != PE_OK) return fail(rc, "%s", err.c_str());
 
     DeviceGuard dg(h->device);
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
-
-    pe::FwdArgs a;
-    memset(&a, 0, sizeof a);
-    a.wpk = h->wpk;
-    a.bias = h->bias32;
-    a.num_cus = h->num_cus;
-    a.E = E;
-    a.m = m;
-    a.order = merge ? 1 : 0;
-
-    if (input_kind == PE_INPUT_PATCHES) {
-        // patch rows: launches of at most kMaxLaunchBytes of input
-        const int64_t rows_per = (int64_t)(kMaxLaunchBytes / (uint64_t)(K * ies));
-        for (int64_t r = 0; r < N; r += rows_per) {
-            const int64_t nr = (N - r < rows_per) ? N - r : rows_per;
-            a.kind = 0;
-            a.wpk = h->wpk_rows;
-            a.plane = (uint32_t)(pe::kTp * P * P);  // a row is [C][Tp][P][P]
-            a.rstr = (uint32_t)P;
-            a.in = static_cast<const char *>(input) + r * K * ies;
-            a.in_bytes = (uint32_t)(nr * K * ies);
-            a.out = static_cast<char *>(out) + r * E * oes;
-            a.addend = addend ? static_cast<const char *>(addend) + r * E * oes : nullptr;
-            a.n_rows = (int32_t)nr;
-            a.n_items = 0;
-            a.colmajor = (uint64_t)nr * K * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
-            hipError_t e = pe::launch_forward(a, P, wes, ies, oes, st);
-            if (e != hipSuccess) return hip_fail(e, "forward launch");
-        }
-        return PE_OK;
-    }
-
-    // frames: launches of at most kMaxItems consecutive items (any number when they are all
-    // alike) and at most kMaxLaunchBytes of input. A launch whose items are all single images loads an image's shared temporal slots
-    // once; images mixed with videos run in the videos' launch (both temporal slots read the
-    // image's one frame, which is exact), since a launch per run of images or videos costs a
-    // launch and a partly idle last round each. With image_fold, single images are kept apart:
-    // only their launches use the folded weight. Items of different frame sizes share a launch
-    // (the kernels then take each item's strides per lane instead of one scalar stride).
-    const bool split_images = cfg.image_fold != 0;
-    int64_t x0 = 0;  // element offset of item i0
-    int i0 = 0;
-    while (i0 < n_items) {
-        int i1 = i0;
-        int64_t span = 0;
-        bool mixed = false, all_images = true, same = true;
-        auto same_as_first = [&](int i) {
-            return F[i] == F[i0] && grid_thw[3 * i] == grid_thw[3 * i0] && grid_thw[3 * i + 1] == grid_thw[3 * i0 + 1] &&
-                   grid_thw[3 * i + 2] == grid_thw[3 * i0 + 2];
-        };
-        while (i1 < n_items && (!split_images || (F[i1] == 1) == (F[i0] == 1)) &&
-               (uint64_t)(span + elems[i1]) * ies <= kMaxLaunchBytes) {
-            const bool still_same = same && same_as_first(i1);
-            // the item table holds kMaxItems entries; launches of identical items never read it
-            // past the first (a row's item is a division), so they may hold more
-            if (i1 - i0 >= pe::kMaxItems && !still_same) break;
-            span += elems[i1];
-            mixed = mixed || grid_thw[3 * i1 + 1] != grid_thw[3 * i0 + 1] || grid_thw[3 * i1 + 2] != grid_thw[3 * i0 + 2];
-            all_images = all_images && F[i1] == 1;
-            same = still_same;
-            ++i1;
-        }
-        a.kind = 1;
-        a.img = all_images ? 1 : 0;
-        a.fold = a.img && cfg.image_fold ? 1 : 0;
-        a.wpk = a.fold ? h->wpk_fold : h->wpk;
-        a.mixg = mixed ? 1 : 0;
-        a.rstr = (uint32_t)grid_thw[3 * i0 + 2] * (uint32_t)P;
-        a.plane = (uint32_t)grid_thw[3 * i0 + 1] * (uint32_t)P * a.rstr;
-        a.in = static_cast<const char *>(input) + x0 * ies;
-        a.in_bytes = (uint32_t)(span * ies);
-        a.out = static_cast<char *>(out) + row0[i0] * E * oes;
-        a.addend = addend ? static_cast<const char *>(addend) + row0[i0] * E * oes : nullptr;
-        a.n_rows = (int32_t)(row0[i1] - row0[i0]);
-        a.n_items = i1 - i0;
-        a.colmajor = (uint64_t)span * ies < (uint64_t)pe::packed_cols(E, ies) * K * ies;
-        a.uni = same ? 1 : 0;
-        a.u_rows = (int32_t)(row0[i0 + 1] - row0[i0]);
-        a.u_elems = (uint32_t)elems[i0];
-        int64_t off = 0;
-        for (int i = i0; i < i1 && i - i0 < pe::kMaxItems; ++i) {
-            pe::Item &it = a.items[i - i0];
-            it.row0 = (int32_t)(row0[i] - row0[i0]);
-            it.t = grid_thw[3 * i];
-            it.h = grid_thw[3 * i + 1];
-            it.w = grid_thw[3 * i + 2];
-            it.F = F[i];
-            it.x_off = (uint32_t)off;
-            off += elems[i];
-        }
-        hipError_t e = pe::launch_forward(a, P, wes, ies, oes, st);
+    const int64_t row_bytes = (int64_t)cfg.embed_dim * rq.out_esz;
+    for (pe::Launch &L : plan) {
+        pe::FwdArgs &a = L.a;
+        a.wpk = L.weight_map == pe::kWeightRows ? h->wpk_rows : (L.weight_map == pe::kWeightFold ? h->wpk_fold : h->wpk);
+        a.bias = h->bias32;
+        a.in = static_cast<const char *>(input) + L.in_off;
+        a.out = static_cast<char *>(out) + L.row0 * row_bytes;
+        a.addend = addend ? static_cast<const char *>(addend) + L.row0 * row_bytes : nullptr;
+        hipError_t e = pe::launch_forward(a, rq.P, rq.weight_esz, rq.in_esz, rq.out_esz, st);
         if (e != hipSuccess) return hip_fail(e, "forward launch");
-        x0 += span;
-        i0 = i1;
     }
     return PE_OK;
 }
@@ -364,6 +281,37 @@ int pe_forward_add(pe_handle h, int32_t input_kind, const void *input, int32_t i
                    void *out, void *hip_stream) {
     if (n_items > 0 && !addend) return fail(PE_ERR_INVALID_ARG, "addend is NULL");
     return forward_impl(h, input_kind, input, in_dtype, grid_thw, frames, n_items, addend, out, hip_stream);
+}
+
+int pe_forward_plan(pe_handle h, int32_t input_kind, int32_t in_dtype, const int32_t *grid_thw,
+                    const int32_t *frames, int32_t n_items, pe_launch_info *info, int32_t max_info) {
+    if (max_info < 0 || (max_info > 0 && !info))
+        return fail(PE_ERR_INVALID_ARG, "info must hold max_info >= 0 entries");
+    const int crc = check_request(h, input_kind, in_dtype, n_items, grid_thw);
+    if (crc != PE_OK) return crc;
+    if (n_items == 0) return 0;
+    pe::PlanRequest rq;
+    fill_request(h, input_kind, in_dtype, grid_thw, frames, n_items, rq);
+    std::vector<pe::Launch> plan;
+    std::string err;
+    const int rc = pe::plan_forward(rq, plan, err);
+    if (rc != PE_OK) return fail(rc, "%s", err.c_str());
+    for (size_t i = 0; i < plan.size() && (int64_t)i < max_info; ++i) {
+        const pe::Launch &L = plan[i];
+        pe_launch_info &o = info[i];
+        memset(&o, 0, sizeof o);
+        snprintf(o.kernel, sizeof o.kernel, "%s", pe::kernel_name(L.tile.id));
+        o.tile_rows = L.tile.bm;
+        o.tile_cols = L.tile.bn;
+        o.workgroups = L.workgroups;
+        o.row0 = L.row0;
+        o.n_rows = L.a.n_rows;
+        o.in_offset = (int64_t)L.in_off;
+        o.in_bytes = L.a.in_bytes;
+        o.n_items = L.a.n_items;
+        o.a_mode = L.a.kind == 0 ? PE_A_PATCH_ROWS : (L.a.fold ? PE_A_FOLDED_IMAGES : (L.a.img ? PE_A_IMAGES : PE_A_FRAMES));
+    }
+    return plan.size() > (size_t)INT32_MAX ? fail(PE_ERR_SHAPE, "too many launches") : (int)plan.size();
 }
 
 int pe_layernorm(const void *x, int32_t dtype, const void *gamma, const void *beta, int32_t param_dtype,

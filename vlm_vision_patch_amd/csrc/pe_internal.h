@@ -6,47 +6,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pe_plan.h"  // FwdArgs, Item, kMaxItems, TileId
+
 namespace pe {
 
 constexpr int kC = 3;          // input channels
 constexpr int kTp = 2;         // temporal patch size
-constexpr int kMaxItems = 64;  // items per launch (the item table travels in the kernel arguments)
-
-// One item (image or video) of a frames launch. Offsets are in input elements relative to the
-// launch's input pointer; rows are relative to the launch's first output row.
-struct Item {
-    int32_t row0;     // first output row of the item
-    int32_t t, h, w;  // patch grid
-    int32_t F;        // frame count
-    uint32_t x_off;   // element offset of the item's first frame
-};
-
-struct FwdArgs {
-    const void *in;      // launch input base
-    const void *wpk;     // packed weight
-    const float *bias;   // fp32 [E] or null
-    void *out;           // launch output base (row 0 of the launch)
-    const void *addend;  // fused add: [rows, E] in the output dtype at the launch's rows, or null
-    uint32_t in_bytes;   // bytes addressable from `in` (buffer range; loads beyond read 0)
-    int32_t n_rows;      // output rows in this launch
-    int32_t E;
-    int32_t kind;        // 0 patch rows, 1 frames
-    int32_t order;       // 0 raster, 1 merge window
-    int32_t m;           // merge size
-    int32_t n_items;
-    int32_t tiles_m, tiles_n;
-    int32_t colmajor;      // tile order within an XCD's run: 1 = column tiles outermost
-    int32_t img;           // 1: frames launch whose items are all single images (F = 1)
-    int32_t fold;          // 1: such a launch reads the folded weight (kAFold)
-    int32_t mixg;          // 1: frames launch whose items differ in frame size (h, w)
-    int32_t num_cus;       // compute units of the device (tile-size choice)
-    uint32_t plane, rstr;  // channel and pixel-row strides (elements) when every item has one frame size
-    // every item of the launch the same (t, h, w, F): item of a row by division, no table lookup
-    int32_t uni;
-    int32_t u_rows;        // rows per item (t*h*w)
-    uint32_t u_elems;      // input elements per item
-    Item items[kMaxItems];
-};
 
 // Fragment map: which patch elements the lane group g (0..3) of k-step s feeds to the matrix
 // core. A fragment is 16 bytes: 8 bf16 or 4 fp32 elements. Pixel rows are indexed
@@ -167,6 +132,25 @@ __host__ __device__ constexpr UFrag tt_frag(int P, int uf) {
 // k-step reads 64 contiguous bytes of each row. Elements at K and beyond are zero in the packed
 // weight (P = 14: the last lane group of step 36).
 __host__ __device__ constexpr int rows_steps(int P) { return (kC * kTp * P * P + 31) / 32; }
+// Where the loads of the rows map go. The raw buffer loads take the per-step part of the address
+// as a scalar offset, which the hardware's range check does not cover, so no load may rely on
+// the range check to stay inside the row: a fragment past the row's K elements (P = 14: lane
+// half 1 of the last sub-step) loads lane half 0's elements instead, which lie inside the row,
+// and the kernel zeroes it.
+//   rows_frag_real: elements [32s + 16j + 8h, +8) are elements of the row (K is a multiple of 8)
+//   rows_load_elem: first element that lane half h actually loads for (s, j)
+__host__ __device__ constexpr bool rows_frag_real(int P, int s, int j, int h) {
+    return 32 * s + 16 * j + 8 * h < kC * kTp * P * P;
+}
+__host__ __device__ constexpr int rows_load_elem(int P, int s, int j, int h) {
+    return rows_frag_real(P, s, j, h) ? 32 * s + 16 * j + 8 * h : 32 * s + 16 * j;
+}
+// The large-tile kernel stages patch rows through LDS in 128-byte pieces, each loaded as eight
+// 16-byte parts. Part q of piece c lies at bytes c*128 + 16q of a row of kb bytes (kb a multiple
+// of 16); a part past the row end loads part 0 of the same piece instead (inside the row, since
+// a piece exists only if it starts inside the row) and is zeroed.
+__host__ __device__ constexpr bool piece_part_real(int kb, int c, int q) { return c * 128 + 16 * q < kb; }
+__host__ __device__ constexpr int piece_load_part(int kb, int c, int q) { return piece_part_real(kb, c, q) ? q : 0; }
 
 // bf16 folded map for single-frame items (opt-in, approximate): both temporal slots of an image read
 // the same frame, so out = x . (W[:, :, 0] + W[:, :, 1]) over the C*P*P elements of one frame. The

@@ -393,21 +393,25 @@ __device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const u
         return MG ? frag_off<P, ISZ>(u, x, vpl[rb], vrs[rb]) : frag_off<P, ISZ>(u, x, plane, rstr);
     };
     if constexpr (AM == kARows) {
-        constexpr int K = kC * kTp * P * P;
+        static_assert((kC * kTp * P * P) % 8 == 0, "a fragment lies wholly inside or outside the row");
         static_for<2>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             constexpr int k0 = 32 * s + 16 * j;  // first element of lane half 0
+            // vb already holds lane half 1's +8 elements; a half-1 fragment past the row loads
+            // half 0's elements (rows_load_elem) and is zeroed: the bytes past a row belong to the
+            // next row (non-finite values there would poison the products even against the zero
+            // weight) or lie past the end of the caller's buffer
+            constexpr bool h1_real = rows_frag_real(P, s, j, 1);
+            static_assert(rows_load_elem(P, s, j, 1) == (h1_real ? k0 + 8 : k0), "rows map placement");
 #pragma unroll
             for (int rb = 0; rb < TM; ++rb) {
-                if constexpr (k0 >= K) {
+                if constexpr (!rows_frag_real(P, s, j, 0)) {
                     zero_frag(dst[rb][j]);
-                } else {
+                } else if constexpr (h1_real) {
                     ld_whole<ISZ>(rsrc, vb[rb], ISZ * k0, dst[rb][j]);
-                    // lanes 32-63 of the last fragment would read past the row: zero (the packed
-                    // weight is zero there too, but the next row's values could be non-finite)
-                    if constexpr (k0 + 8 >= K) {
-                        if (h) zero_frag(dst[rb][j]);
-                    }
+                } else {
+                    ld_whole<ISZ>(rsrc, h ? vb[rb] - 8u * ISZ : vb[rb], ISZ * k0, dst[rb][j]);
+                    if (h) zero_frag(dst[rb][j]);
                 }
             }
         });
@@ -826,6 +830,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     // Patch rows: thread piece loads. Load i of a piece: row (i*NT + tid) / 8 of the tile, its
     // 16-byte part (i*NT + tid) % 8; rows past the end read row 0 of the launch (never stored).
     constexpr int KB = kC * kTp * P * P * ISZ;     // bytes of one patch row
+    static_assert(KB % 16 == 0, "a 16-byte part lies wholly inside or outside the row");
     uint32_t av[AST ? AL : 1];
     int apart[AST ? AL : 1];
     if constexpr (AST) {
@@ -841,10 +846,16 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         constexpr int c = decltype(cc)::value;
 #pragma unroll
         for (int i = 0; i < AL; ++i) {
-            dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)av[i], c * 128, 0);
-            // bytes past the row (the last piece) belong to the next row: zero them
             if constexpr (c * 128 + 128 > KB) {
-                if (c * 128 + apart[i] * 16 >= KB) dst[i] = u32x4{0u, 0u, 0u, 0u};
+                // the last piece: a part past the row loads the piece's part 0 (piece_load_part,
+                // inside the row; the bytes past a row belong to the next row or lie past the
+                // caller's buffer) and is zeroed
+                const bool real = piece_part_real(KB, c, apart[i]);
+                dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(real ? av[i] : av[i] - (uint32_t)apart[i] * 16u),
+                                                               c * 128, 0);
+                if (!real) dst[i] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)av[i], c * 128, 0);
             }
         }
     };
@@ -1234,20 +1245,18 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
 // Launchers
 // ----------------------------------------------------------------------------------------
 template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
-inline hipError_t launch16(FwdArgs a, hipStream_t st) {
+inline hipError_t launch16(const FwdArgs &a, hipStream_t st) {
     constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
-    a.tiles_m = (a.n_rows + BM - 1) / BM;
-    a.tiles_n = (a.E + BN - 1) / BN;
+    if (a.tiles_m != (a.n_rows + BM - 1) / BM || a.tiles_n != (a.E + BN - 1) / BN) return hipErrorInvalidValue;
     hipLaunchKernelGGL((pe_fwd16_kernel<P, ESZ, OSZ, TM, TN, WM, WN, KS, PF, AD>), dim3(a.tiles_m * a.tiles_n),
                        dim3(WM * WN * 64), 0, st, a);
     return hipGetLastError();
 }
 
 template <int P, int ISZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD>
-inline hipError_t launch32(FwdArgs a, hipStream_t st) {
+inline hipError_t launch32(const FwdArgs &a, hipStream_t st) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-    a.tiles_m = (a.n_rows + BM - 1) / BM;
-    a.tiles_n = (a.E + BN - 1) / BN;
+    if (a.tiles_m != (a.n_rows + BM - 1) / BM || a.tiles_n != (a.E + BN - 1) / BN) return hipErrorInvalidValue;
     const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
     if (a.kind == 0)
         hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kARows, false>), grid, block, 0, st, a);
@@ -1267,10 +1276,9 @@ inline hipError_t launch32(FwdArgs a, hipStream_t st) {
 }
 
 template <int P, int ISZ, int OSZ, int TM, int TN, int AD>
-inline hipError_t launch_sk(FwdArgs a, hipStream_t st) {
+inline hipError_t launch_sk(const FwdArgs &a, hipStream_t st) {
     constexpr int BM = TM * 32, BN = TN * 32;
-    a.tiles_m = (a.n_rows + BM - 1) / BM;
-    a.tiles_n = (a.E + BN - 1) / BN;
+    if (a.tiles_m != (a.n_rows + BM - 1) / BM || a.tiles_n != (a.E + BN - 1) / BN) return hipErrorInvalidValue;
     const dim3 grid(a.tiles_m * a.tiles_n), block(256);
     if (a.kind == 0)
         hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kARows, false>), grid, block, 0, st, a);
@@ -1289,44 +1297,31 @@ inline hipError_t launch_sk(FwdArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Tile choice. A launch runs in rounds of at most one workgroup per CU; the cost of a round was
-// measured per tile shape (bf16, P = 14, 1k to 332k patches): 256 x 256 tiles ~30 us, 256 x 128
-// ~18 us, split-k 32 x 160 ~8 us. The shape with the fewest (rounds x round cost) wins; ties go to
-// the larger tile (better per area when the chip is full).
-// returns 0: 256 x 256, 1: 256 x 128, 2: split-k
-__host__ inline int choose_tiles(int64_t n_rows, int E, int num_cus) {
-    const int64_t ncu = num_cus > 0 ? num_cus : 256;
-    auto rounds = [&](int64_t tiles) { return (tiles + ncu - 1) / ncu; };
-    const int64_t rt = (n_rows + 255) / 256;
-    const int skn = E % 160 == 0 ? 160 : 128;
-    const int64_t c256 = rounds(rt * ((E + 255) / 256)) * 30;
-    const int64_t c128 = rounds(rt * ((E + 127) / 128)) * 18;
-    const int64_t csk = rounds(((n_rows + 31) / 32) * ((E + skn - 1) / skn)) * 8;
-    if (c256 <= c128 && c256 <= csk) return 0;
-    if (c128 <= csk) return 1;
-    return 2;
-}
-
 // ESZ: weight element size; ISZ: input element size (fp32 input meets a bf16 weight by rounding
 // on load)
 template <int P, int ESZ, int ISZ, int OSZ>
 inline hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
+    // the plan (pe_plan.cpp) chose the kernel and its tile; the launchers recompute the tile
+    // counts from their own template shapes and refuse a launch whose shape differs
+    const int skn = a.E % 160 == 0 ? 160 : 128;
     if constexpr (ESZ == 4) {
         // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps); 32 x 160
         // tiles where E allows (1024 x 1280 makes 256 of them: one round, where 32 x 128 tiles
         // take 1.25; measured 38 us against 45-47 us), one weight k-step per LDS buffer
-        if (a.E % 160 == 0) return launch16<P, ESZ, OSZ, 1, 5, 2, 2, 1, 2, 2>(a, st);
+        if (a.tiles != kTileF32) return hipErrorInvalidValue;
+        if (skn == 160) return launch16<P, ESZ, OSZ, 1, 5, 2, 2, 1, 2, 2>(a, st);
         return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
     } else {
         // 8 waves of 32 x BN (two per SIMD), one weight k-step per LDS buffer (a barrier per k-step
         // measured ~2% faster than two), eight weight fragments read ahead
-        switch (choose_tiles(a.n_rows, a.E, a.num_cus)) {
-            case 0: return launch32<P, ISZ, OSZ, 1, 8, 8, 1, 1, 8, 2, 3>(a, st);
-            case 1: return launch32<P, ISZ, OSZ, 1, 4, 8, 1, 1, 8, 2, 3>(a, st);
-            default:
+        switch (a.tiles) {
+            case kTileLarge256: return launch32<P, ISZ, OSZ, 1, 8, 8, 1, 1, 8, 2, 3>(a, st);
+            case kTileLarge128: return launch32<P, ISZ, OSZ, 1, 4, 8, 1, 1, 8, 2, 3>(a, st);
+            case kTileSplitK:
                 // few rows: split-K workgroups, 32 rows by 160 (or 128) columns
-                if (a.E % 160 == 0) return launch_sk<P, ISZ, OSZ, 1, 5, 2>(a, st);
+                if (skn == 160) return launch_sk<P, ISZ, OSZ, 1, 5, 2>(a, st);
                 return launch_sk<P, ISZ, OSZ, 1, 4, 2>(a, st);
+            default: return hipErrorInvalidValue;
         }
     }
 }
