@@ -5,7 +5,7 @@ A step is one PatchEmbed forward (gather + matrix product + epilogue, one kernel
 K steps captured back to back in a HIP graph and replayed once, bracketed by HIP events on the
 stream they run on; `eager_ms_per_step` gives the same K steps launched one by one from Python.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--extra 5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--extra 2,3]
 """
 from __future__ import annotations
 
@@ -51,31 +51,8 @@ def algorithmic(wl, rows=False, add=False):
     return n, flops, byts
 
 
-def dominant_kernel(wl, num_cus=256):
-    """Name of the kernel that does the step's work, by the library's tile choice for the largest
-    launch (items that are all alike share one launch, others go 64 to a launch): in rounds of one
-    workgroup per CU, 256 x 256 tiles cost ~30 us a round, 256 x 128 ~18 us and split-k ~8 us; the
-    fewest (rounds x cost) wins. fp32 runs the 16x16 kernel."""
-    if wl.w_dtype != "bf16":
-        return "pe_fwd16_kernel"
-    rows = [t * h * w for (t, h, w) in wl.grid]
-    frames = list(wl.frames) or [None] * len(rows)
-    if all(tuple(g) == tuple(wl.grid[0]) and f == frames[0] for g, f in zip(wl.grid, frames)):
-        n = sum(rows)
-    else:
-        n = max(sum(rows[i:i + 64]) for i in range(0, len(rows), 64))
-    E = wl.embed
-    rounds = lambda tiles: -(-tiles // num_cus)
-    rt = -(-n // 256)
-    skn = 160 if E % 160 == 0 else 128
-    c256 = rounds(rt * -(-E // 256)) * 30
-    c128 = rounds(rt * -(-E // 128)) * 18
-    csk = rounds(-(-n // 32) * -(-E // skn)) * 8
-    return "pe_fwd32_kernel" if min(c256, c128) <= csk else "pe_fwd32_sk_kernel"
-
-
 def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=10, cold=False, add=False,
-                  fold=False):
+                  fold=False, keep_out=False):
     """rows: feed the workload's patches as pre-flattened rows [N, K] (the processor's
     pixel_values layout) instead of its frames: same N, weight and bias, synthetic N(0, 1) rows.
     items: keep only the first `items` items (one GPU's share of an item split).
@@ -83,7 +60,11 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     cold: also time single launches after overwriting a 1 GiB buffer (L2 and the 256 MB
     Infinity Cache hold nothing of the inputs), median of `reps`.
     add: fuse the add of a synthetic [N, E] tensor (position embeddings) into the epilogue.
-    fold: the approximate image-fold mode (single-frame items on W[:, :, 0] + W[:, :, 1] in bf16)."""
+    fold: the approximate image-fold mode (single-frame items on W[:, :, 0] + W[:, :, 1] in bf16).
+    keep_out: also return the output of the last timed step (and the inputs, on the host), for the
+    parity check of the timed output.
+    The result holds the library's launch plan of one step (pe_forward_plan): which kernel runs,
+    its tile and grid."""
     import torch
     import workloads
     import vlm_vision_patch_amd as pe
@@ -100,9 +81,11 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     if rows:
         x = workloads.random_tensor((n, wl.k), seed=1000 + idx, dtype=workloads.DTYPES[wl.in_dtype])
         kind, grid, frames = "patches", [[1, 1, n]], None
+    host_in = (x, w, b) if keep_out else None
     x, w = x.to(dev), w.to(dev)
     b = b.to(dev) if b is not None else None
     mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype], image_fold=fold)
+    plan = mod.plan(grid, frames, kind=kind, in_dtype=x.dtype)
     out = torch.empty((n, wl.embed), dtype=workloads.DTYPES[wl.out_dtype], device=dev)
     addend = None
     if add:
@@ -165,7 +148,8 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
         del flush
     mod.close()
     return dict(wl=wl, n=n, flops=flops, bytes=byts, ms=ms, eager_ms=eager_ms, timing=timing, rows=rows,
-                stats=stats, cold_ms=cold_ms)
+                stats=stats, cold_ms=cold_ms, plan=plan, out=out if keep_out else None, host_in=host_in,
+                kind=kind, grid=grid, frames=frames)
 
 
 def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6, eager=False):
@@ -282,33 +266,115 @@ def time_linear_context(idx, steps=20):
             "tflops": round(2.0 * n * wl.k * wl.embed / (ms / 1e3) / 1e12, 2), "steps": steps}
 
 
-def cpu_baseline(idx, min_seconds=10.0):
-    """The oracle, as it stands, timed on this host on repeats of the whole workload (or on its
-    first rows when one pass would exceed the bound)."""
-    import workloads
-    import oracle
-    wl = workloads.WORKLOADS[idx]
-    x, w, b = workloads.generate(wl)
-    n = sum(t * h * ww for (t, h, ww) in wl.grid)
-    threads = max(1, min(os.cpu_count() or 1, 16))
-    rows = None
-    per_row = 2.0 * wl.k * wl.embed
-    if n * per_row > 2e11:      # more than ~30 s on 16 cores: time the first rows only
-        rows = list(range(int(2e11 / per_row)))
-    done, t0 = 0, time.perf_counter()
-    reps = 0
-    while True:
-        oracle.forward(x, w, b, grid=wl.grid, frames=list(wl.frames) or None, kind=wl.kind,
-                       order=wl.order, rows=rows, threads=threads)
-        done += n if rows is None else len(rows)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or rows is not None:
+def cpu_info():
+    """The host's CPU model and how many cores this process may use: the smallest of the affinity
+    mask and the cgroup CPU quota (a container's CPU share), next to what os.cpu_count() says."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    nproc = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = nproc
+    quota = None
+    for path in ("/sys/fs/cgroup/cpu.max",):
+        try:
+            q, per = open(path).read().split()[:2]
+            if q != "max":
+                quota = max(1, math.ceil(int(q) / int(per)))
+        except (OSError, ValueError):
+            pass
+    if quota is None:
+        try:
+            q = int(open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us").read())
+            per = int(open("/sys/fs/cgroup/cpu/cpu.cfs_period_us").read())
+            if q > 0:
+                quota = max(1, math.ceil(q / per))
+        except (OSError, ValueError):
+            pass
+    usable = min(affinity, quota) if quota else affinity
+    return {"model": model, "nproc": nproc, "affinity": affinity, "cgroup_quota": quota, "usable": usable}
+
+
+def sample_rows(n, count, tile=256, seed=0):
+    """A deterministic sample of `count` output rows of n (all rows if count >= n): the first and
+    last rows, the rows on both sides of `tile`-row boundaries (up to a quarter of the sample), then
+    evenly spread rows with a seeded jitter, topped up with seeded random rows where those collide."""
+    import random
+    if count >= n:
+        return list(range(n))
+    rng = random.Random(seed)
+    picked = {0, n - 1}
+    for edge in range(tile, n, tile):
+        if len(picked) + 2 > count // 4:
             break
-    sample = ("%d passes over all %d rows" % (reps, n)) if rows is None else \
-        ("first %d of %d rows" % (len(rows), n))
-    return {"value": done / el, "unit": "patches/s", "cores": threads, "kind": "oracle",
-            "sample": "%s of %s (fp64 direct Conv3d, %d threads, %.1f s)" % (sample, wl.name, threads, el)}
+        picked.update((edge - 1, edge))
+    left = count - len(picked)
+    step = n / max(1, left)
+    for i in range(left):
+        picked.add(min(n - 1, int(i * step + rng.random() * step)))
+    while len(picked) < count:
+        picked.add(rng.randrange(n))
+    return sorted(picked)
+
+
+def cpu_baseline(r, target_seconds=15.0):
+    """The oracle, as it stands, timed on this host over a bounded sample of the workload's output
+    rows (about `target_seconds` of CPU work, on every core this process may use), and the same rows
+    of the timed GPU output compared with it (the parity of what was timed)."""
+    import numpy as np
+    import oracle
+    wl = r["wl"]
+    x, w, b = r["host_in"]
+    info = cpu_info()
+    threads = info["usable"]
+    n = r["n"]
+    kw = dict(grid=r["grid"], frames=r["frames"], kind=r["kind"], order=wl.order, threads=threads)
+    # exact fp64 copies once (the oracle would convert the whole input on every call), then the
+    # stratified sample in chunks, in an order that spreads every prefix over the whole workload,
+    # until the time bound or the end of the sample
+    xd, wd, bd = oracle._f64(x), oracle._f64(w), (oracle._f64(b) if b is not None else None)
+    order_rows = sample_rows(n, min(n, 400000), seed=2)
+    perm = np.random.default_rng(3).permutation(len(order_rows))
+    rows, refs = [], []
+    t0 = time.perf_counter()
+    chunk = 4 * threads
+    done = 0
+    while done < len(order_rows):
+        part = sorted(order_rows[i] for i in perm[done:done + chunk])
+        refs.append(oracle.forward(xd, wd, bd, rows=part, **kw))
+        rows += part
+        done += len(part)
+        el = time.perf_counter() - t0
+        if el >= target_seconds:
+            break
+        chunk = min(8192, chunk * 2)
+    el = time.perf_counter() - t0
+    ref = np.concatenate(refs)
+    import torch
+    got = r["out"].index_select(0, torch.tensor(rows, device=r["out"].device)).float().cpu().double().numpy()
+    err = np.abs(got - ref)
+    if wl.out_dtype == "bf16":
+        tol, tol_text = 1e-3 + 1e-2 * np.abs(ref), "|err| <= 1e-3 + 1e-2 |ref|"
+    else:
+        tol, tol_text = 5e-4, "|err| <= 5e-4"
+    bad = int((err > tol).sum())
+    sample = ("%s %d of the %d output rows of %s (drawn from a stratified sample: the first and last rows, both "
+              "sides of 256-row tile edges, the rest spread evenly): fp64 direct Conv3d, %d threads, %.1f s" % (
+                  "all" if len(rows) == n else "a sample of", len(rows), n, wl.name, threads, el))
+    cpu = {"value": round(len(rows) / el, 1), "unit": "patches/s", "cores": threads, "kind": "oracle",
+           "sample": sample, "cpu_model": info["model"], "nproc": info["nproc"],
+           "cores_note": "cores = min(affinity mask %d, cgroup CPU quota %s) of the %d the host has" % (
+               info["affinity"], info["cgroup_quota"], info["nproc"])}
+    parity = {"rows_checked": len(rows), "max_abs_err": float(err.max()), "out_of_tolerance": bad,
+              "tolerance": tol_text}
+    return cpu, parity
 
 
 def load_traffic(kernel, workload):
@@ -327,6 +393,51 @@ def load_traffic(kernel, workload):
     return None
 
 
+def pmc_per_dispatch(csv_dir, counter, kernel):
+    """Mean over dispatches of `counter` for kernels whose name contains `kernel`, from the
+    counter-collection CSV files rocprofv3 --pmc wrote under csv_dir (a dispatch's value is the sum
+    of its rows: one per counter instance), and the dispatch count."""
+    import csv
+    per = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter or kernel not in row.get("Kernel_Name", ""):
+                    continue
+                key = (path, row.get("Dispatch_Id"))
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit("no %s rows for kernel %s under %s" % (counter, kernel, csv_dir))
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_pmc(workload, kernel, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes, name=None):
+    """HBM bytes per launch of `kernel` on `workload` from two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE, in KiB per dispatch), each scaled by what the same counter read for one plain device
+    copy of cal_bytes bytes (bench.py --copy-calibrate), into profiles/traffic.json under the current
+    kernel sources hash."""
+    import workloads
+    wl = workloads.WORKLOADS[workload]
+    _, _, alg = algorithmic(wl)
+    fk, nf = pmc_per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
+    wk, nw = pmc_per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    cf, _ = pmc_per_dispatch(cal_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw, _ = pmc_per_dispatch(cal_write_dir, "WRITE_SIZE", "copyBuffer")
+    ff, wf = cal_bytes / (cf * 1024.0), cal_bytes / (cw * 1024.0)
+    total = fk * 1024.0 * ff + wk * 1024.0 * wf
+    rec = {"kernel_hash": kernel_hash(), "kernel": kernel, "fetch_kib_per_launch": round(fk, 1),
+           "write_kib_per_launch": round(wk, 1), "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+           "bytes_per_launch": int(round(total)), "algorithmic_bytes_per_launch": alg,
+           "launches_counted": min(nf, nw)}
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    d = json.load(open(p)) if os.path.exists(p) else {}
+    d[name or wl.name] = rec
+    with open(p, "w") as f:
+        json.dump(d, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
 def workloads_name(idx):
     import workloads
     return workloads.WORKLOADS[idx].name
@@ -337,8 +448,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--extra", type=str, default="5,5r,5a,5n,5f,2f,5s8,3,4,6,1",
+    ap.add_argument("--workload", type=int, default=5,
+                    help="the headline workload (default 5: 64 images of 1008 x 1008, 331,776 patches, the "
+                         "largest configuration and the one the bf16 matrix-core fraction is quoted on)")
+    ap.add_argument("--extra", type=str, default="2,5r,5a,5n,5f,2f,5s8,3,4,6,1",
                     help="comma-separated further workloads reported under 'also' ('' for none); "
                          "a trailing r feeds that workload's patches as pre-flattened rows, a trailing "
                          "a fuses the add of an [N, E] tensor, a trailing n times the PatchMerger "
@@ -351,7 +464,16 @@ def main():
                     help="time K launches from Python instead of a captured graph (for counter runs)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
                     help="only run one plain device-to-device copy of BYTES (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=7, metavar=("WORKLOAD", "KERNEL", "FETCH_DIR", "WRITE_DIR",
+                                                          "CAL_FETCH_DIR", "CAL_WRITE_DIR", "CAL_BYTES"),
+                    help="no GPU work: write the HBM bytes per launch of KERNEL on WORKLOAD from rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE output directories, calibrated by a copy's counters, "
+                         "into profiles/traffic.json")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        w_, k_, fd, wd, cfd, cwd, cb = args.summarize_pmc
+        print(json.dumps(summarize_pmc(int(w_), k_, fd, wd, cfd, cwd, int(cb))), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py times one GPU only; --gpus %d is not supported (PatchEmbed rows are independent: "
               "across GPUs the items are dealt out, one handle per device, with no exchange)" % args.gpus,
@@ -373,7 +495,9 @@ def main():
         print(json.dumps({"copy_bytes": n * 4}), flush=True)
         return
 
-    r = time_workload(args.workload, args.steps, args.warmup, graph=not args.eager, cold=not args.eager)
+    cpu_leg = not args.no_cpu and not args.eager
+    r = time_workload(args.workload, args.steps, args.warmup, graph=not args.eager, cold=not args.eager,
+                      keep_out=cpu_leg)
     wl = r["wl"]
     t_s = r["ms"] / 1e3
     tflops = r["flops"] / t_s / 1e12
@@ -383,7 +507,11 @@ def main():
     ai = r["flops"] / r["bytes"]
     ridge = peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9)
     bound = "mfma" if ai >= ridge else "hbm"
-    kname = dominant_kernel(wl, torch.cuda.get_device_properties(0).multi_processor_count)
+    # the kernel that does the step's work, as the library planned it (pe_forward_plan): the launch
+    # with the most output rows; the step's HIP-event time covers all of its launches
+    plan = r["plan"]
+    dom = max(plan, key=lambda L: L["n_rows"])
+    kname = dom["kernel"]
     traffic = load_traffic(kname, wl.name)
     roof = {"bound": bound,
             "achieved": round(tflops if bound == "mfma" else gbs, 3),
@@ -392,8 +520,11 @@ def main():
             "frac": round((tflops / peak_fl) if bound == "mfma" else (gbs / PEAK_HBM_GBS), 4),
             "traffic": traffic,
             "kernel": kname,
+            "launch": {"tile": dom["tile"], "workgroups": dom["workgroups"], "a_mode": dom["a_mode"],
+                       "launches_per_step": len(plan)},
             "per_launch": {"flops": r["flops"], "alg_bytes": r["bytes"], "avg_us": round(r["ms"] * 1e3, 3)},
-            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "frac_roofline_model": round(tflops / min(peak_fl, ai * PEAK_HBM_GBS / 1e3), 4)}
     also = {}
     for spec in [v.strip() for v in args.extra.split(",") if v.strip()]:
         if spec.endswith("n"):
@@ -413,18 +544,23 @@ def main():
                           fold=fold)
         qt = q["ms"] / 1e3
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
+        qai = q["flops"] / q["bytes"]
+        qdom = max(q["plan"], key=lambda L: L["n_rows"])
         also[q["wl"].name + ("_as_patch_rows" if as_rows else "") + ("_plus_pos_embed" if with_add else "")
              + ("_image_fold_approx" if fold else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
                               "tflops": round(q["flops"] / qt / 1e12, 2),
                               "frac_matrix_peak": round(q["flops"] / qt / 1e12 / qpk, 4),
                               "frac_hbm": round(q["bytes"] / qt / 1e9 / PEAK_HBM_GBS, 4),
+                              # against the roofline model min(peak, AI x HBM bandwidth)
+                              "frac_roofline_model": round(q["flops"] / qt / 1e12 / min(qpk, qai * PEAK_HBM_GBS / 1e3), 4),
+                              "kernel": qdom["kernel"], "tile": qdom["tile"], "launches_per_step": len(q["plan"]),
                               "n_patches": q["n"], "steps": st,
                               **({"approximate": "image fold: W[:, :, 0] + W[:, :, 1] rounded to bf16 once; "
                                                  "tflops counts the nominal Conv3d FLOPs, the matrix cores do "
                                                  "about half for images"} if fold else {})}
     if not args.no_context and not args.eager:
         also["context_library_gemm_" + workloads_name(5)] = time_linear_context(5)
-    cpu = None if args.no_cpu else cpu_baseline(args.workload)
+    cpu, parity = cpu_baseline(r) if cpu_leg else (None, None)
     line = {
         "metric": METRIC, "value": round(r["n"] / t_s, 1), "unit": "patches/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms"], 6),
@@ -439,7 +575,9 @@ def main():
         "eager_ms_per_step": round(r["eager_ms"], 6),
         "timing": r["timing"], "timing_stats": r["stats"],
         "cold_ms_per_step": round(r["cold_ms"], 6) if r["cold_ms"] is not None else None,
-        "roofline": roof, "cpu_baseline": cpu, "also": also,
+        "roofline": roof, "cpu_baseline": cpu,
+        "parity_max_err": parity["max_abs_err"] if parity else None, "parity": parity,
+        "also": also,
     }
     print(json.dumps(line), flush=True)
 

@@ -1,6 +1,8 @@
 """CPU checks of bench.py's host-side arithmetic: the algorithmic FLOPs and bytes of each workload
-(the units behind `roofline.achieved` and `hbm_frac`), the kernel it names as doing the work, and
-the refusal of more than one GPU."""
+(the units behind `roofline.achieved` and `hbm_frac`), the row sample of the CPU baseline and its
+parity check, the counter summary behind `roofline.traffic`, and the refusal of more than one GPU.
+The kernel the bench names comes from the library's own launch plan (pe_forward_plan), tested in
+test_plan.py and on the GPU."""
 import os
 import subprocess
 import sys
@@ -47,11 +49,43 @@ def test_algorithmic_units_of_variants():
     assert add_bytes - byts == n * 1280 * 2
 
 
-@pytest.mark.parametrize("idx,kernel", [(1, "pe_fwd16_kernel"), (2, "pe_fwd32_sk_kernel"),
-                                        (3, "pe_fwd32_sk_kernel"), (4, "pe_fwd32_kernel"),
-                                        (5, "pe_fwd32_kernel"), (6, "pe_fwd32_kernel")])
-def test_dominant_kernel(idx, kernel):
-    assert bench.dominant_kernel(workloads.WORKLOADS[idx]) == kernel
+def test_sample_rows_cover_edges_and_spread():
+    n = 331776
+    rows = bench.sample_rows(n, 5000)
+    assert rows == sorted(set(rows)) and len(rows) == 5000 and rows[0] == 0 and rows[-1] == n - 1
+    assert {255, 256, 511, 512} <= set(rows)
+    # evenly spread: every 1/50 of the rows holds some of the sample
+    assert all(any(i * n // 50 <= r < (i + 1) * n // 50 for r in rows) for i in range(50))
+    assert bench.sample_rows(100, 1000) == list(range(100))
+
+
+def test_cpu_info_states_model_and_share():
+    info = bench.cpu_info()
+    assert info["usable"] >= 1 and info["usable"] <= info["nproc"]
+    assert isinstance(info["model"], str)
+
+
+def test_summarize_pmc_reads_rocprof_csv(tmp_path, monkeypatch):
+    """Per-dispatch sums of a counter's instance rows, averaged over dispatches, scaled by a copy."""
+    hdr = "Correlation_Id,Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+
+    def write(d, rows):
+        os.makedirs(d, exist_ok=True)
+        open(os.path.join(d, "pmc_counter_collection.csv"), "w").write(hdr + "".join(rows))
+    k = "void pe::pe_fwd32_kernel<14>(pe::FwdArgs)"
+    write(str(tmp_path / "f"), ['1,1,"%s",FETCH_SIZE,100\n' % k, '1,1,"%s",FETCH_SIZE,50\n' % k,
+                                '2,2,"%s",FETCH_SIZE,150\n' % k, '3,3,other,FETCH_SIZE,999\n'])
+    write(str(tmp_path / "w"), ['1,1,"%s",WRITE_SIZE,200\n' % k, '2,2,"%s",WRITE_SIZE,200\n' % k])
+    write(str(tmp_path / "cf"), ['1,1,__amd_rocclr_copyBuffer,FETCH_SIZE,512\n'])
+    write(str(tmp_path / "cw"), ['1,1,__amd_rocclr_copyBuffer,WRITE_SIZE,1024\n'])
+    assert bench.pmc_per_dispatch(str(tmp_path / "f"), "FETCH_SIZE", "pe_fwd32_kernel") == (150.0, 2)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    rec = bench.summarize_pmc(5, "pe_fwd32_kernel", str(tmp_path / "f"), str(tmp_path / "w"),
+                              str(tmp_path / "cf"), str(tmp_path / "cw"), 1024 * 1024)
+    # copy of 1 MiB: fetch reads 512 KiB (factor 2), write 1024 KiB (factor 1)
+    assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
+    assert rec["bytes_per_launch"] == 150 * 1024 * 2 + 200 * 1024
 
 
 def test_more_than_one_gpu_is_refused():

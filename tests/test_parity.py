@@ -107,6 +107,35 @@ def test_workload_5_sampled(pe):
     print("%s: %d sampled rows, max err %.3g" % (wl.name, len(rows), e), flush=True)
 
 
+@pytest.mark.timeout(1200)
+def test_workload_5_all_rows(pe):
+    """Every one of the 331,776 x 1280 outputs of the 64-image batch (the configuration the
+    benchmark reports), element by element, in the benchmark's launch configuration: the oracle runs
+    in chunks of four images' rows so that host memory stays bounded (N = t*h*w per item, items
+    concatenated: "freechatgpt/mytransformer" section 3.2)."""
+    import bench
+    wl = workloads.WORKLOADS[5]
+    x, w, b = workloads.generate(wl)
+    n = sum(t * h * ww for (t, h, ww) in wl.grid)
+    say("%s: all %d rows, oracle in chunks of 20736 rows" % (wl.name, n))
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV), order=wl.order, out_dtype=torch.bfloat16)
+    out = mod(x.to(DEV), list(wl.grid), list(wl.frames))
+    torch.cuda.synchronize()
+    mod.close()
+    # exact fp64 copies once, so that the chunks do not convert the inputs again
+    xd, wd, bd = oracle._f64(x), oracle._f64(w), oracle._f64(b)
+    threads = bench.cpu_info()["usable"]
+    chunk, worst = 4 * 5184, 0.0
+    for r0 in range(0, n, chunk):
+        rows = np.arange(r0, min(n, r0 + chunk), dtype=np.int64)
+        ref = oracle.forward(xd, wd, bd, grid=list(wl.grid), frames=list(wl.frames), order=wl.order, rows=rows,
+                             threads=threads)
+        got = out[r0:r0 + len(rows)].float().cpu().double().numpy()
+        worst = max(worst, check(got, ref, torch.bfloat16, "%s rows %d..%d" % (wl.name, r0, r0 + len(rows) - 1)))
+        print("rows %d..%d ok (max err so far %.3g)" % (r0, r0 + len(rows) - 1, worst), flush=True)
+    print("%s: all %d rows within 1e-3 + 1e-2|ref|, max err %.3g" % (wl.name, n, worst), flush=True)
+
+
 def test_workload_6_sampled(pe):
     """The Qwen3-VL-2B-shaped workload (P16, E1024, bias) over items of mixed sizes: every item's
     first and last rows plus a seeded sample."""
@@ -755,4 +784,54 @@ def test_graph_replays_match_eager(pe):
         other = mod(xd, list(wl.grid), list(wl.frames))     # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(other, eager)
+    mod.close()
+
+
+def test_forward_plan_names_the_launches(pe):
+    """pe_forward_plan on a live handle: the launches the benchmark reports for each workload, and
+    the same request checks and codes as pe_forward."""
+    say("pe_forward_plan on workloads 1-6 and on bad requests")
+    expect = {1: ("pe_fwd16_kernel", 1), 2: ("pe_fwd32_sk_kernel", 1), 3: ("pe_fwd32_sk_kernel", 1),
+              4: ("pe_fwd32_kernel", 1), 5: ("pe_fwd32_kernel", 1), 6: ("pe_fwd32_kernel", 1)}
+    for idx, (kname, nl) in expect.items():
+        wl = workloads.WORKLOADS[idx]
+        _, w, b = workloads.generate(wl)
+        mod = pe.PatchEmbed(w.to(DEV), b.to(DEV) if b is not None else None, order=wl.order,
+                            out_dtype=workloads.DTYPES[wl.out_dtype])
+        plan = mod.plan(list(wl.grid), list(wl.frames) or None, kind=wl.kind,
+                        in_dtype=workloads.DTYPES[wl.in_dtype])
+        assert [L["kernel"] for L in plan] == [kname] * nl, (idx, plan)
+        assert sum(L["n_rows"] for L in plan) == sum(t * h * ww for (t, h, ww) in wl.grid)
+        if idx == 5:
+            assert plan[0]["tile"] == [256, 256] and plan[0]["workgroups"] == 6480 and plan[0]["a_mode"] == "images"
+        if idx == 2:
+            assert plan[0]["tile"] == [32, 160] and plan[0]["workgroups"] == 256
+        if wl.order == "merge":
+            with pytest.raises(pe.PEError) as e1:
+                mod.plan([[1, 3, 5]], [1])           # merge order needs even h and w (frames)
+            assert e1.value.code == pe.PE_ERR_SHAPE
+        with pytest.raises(pe.PEError) as e2:
+            mod.plan([[2, 4, 4]], [1])               # one frame cannot make two temporal patches
+        assert e2.value.code == pe.PE_ERR_SHAPE
+        mod.close()
+
+
+def test_call_on_a_side_stream(pe):
+    """stream= names a stream other than the current one: the output and the input's contiguous copy
+    that the binding allocates are marked as used on that stream, and the result is right."""
+    say("PatchEmbed on a side stream, non-contiguous input, binding-allocated output")
+    P, E = 14, 256
+    g = [[1, 6, 8]]
+    x = workloads.random_tensor((3, 6 * P, 8 * P), seed=8100, dtype=torch.bfloat16)
+    w = workloads.random_tensor((E, 3, 2, P, P), seed=8101, dtype=torch.bfloat16, dist="uniform", bound=0.03)
+    mod = pe.PatchEmbed(w.to(DEV), None, order="merge")
+    side = torch.cuda.Stream(device=DEV)
+    xt = x.to(DEV).transpose(1, 2).contiguous().transpose(1, 2)   # same values, not contiguous
+    assert not xt.is_contiguous()
+    torch.cuda.synchronize()
+    out = mod(xt, g, [1], stream=side.cuda_stream)
+    side.synchronize()
+    got = out.float().cpu().double().numpy()
+    ref = oracle.forward(x, w, None, grid=g, frames=[1], order="merge")
+    check(got, ref, torch.bfloat16, "side stream")
     mod.close()
