@@ -438,6 +438,14 @@ def summarize_pmc(workload, kernel, fetch_dir, write_dir, cal_fetch_dir, cal_wri
     return rec
 
 
+def parse_extra(spec):
+    """One --extra entry: (workload, as patch rows, fused add, image fold, items kept or None).
+    '5r' patch rows, '5a' fused add, '5f' fold, '5s8' the first 8 items."""
+    as_rows, with_add, fold = spec.endswith("r"), spec.endswith("a"), spec.endswith("f")
+    share = int(spec.split("s")[1]) if "s" in spec else None
+    return int(spec.rstrip("raf").split("s")[0]), as_rows, with_add, fold, share
+
+
 def workloads_name(idx):
     import workloads
     return workloads.WORKLOADS[idx].name
@@ -532,12 +540,8 @@ def main():
             also[workloads_name(e) + "_merger_layernorm"] = time_merger_front(e, max(5, min(args.steps, 50)),
                                                                                eager=args.eager)
             continue
-        as_rows = spec.endswith("r")
-        with_add = spec.endswith("a")
-        fold = spec.endswith("f")
-        share = int(spec.split("s")[1]) if "s" in spec else None
-        e = int(spec.rstrip("raf").split("s")[0])
-        if e == args.workload and not as_rows and share is None and not fold:
+        e, as_rows, with_add, fold, share = parse_extra(spec)
+        if e == args.workload and not (as_rows or with_add or fold or share is not None):
             continue
         st = max(5, min(args.steps, 50))
         q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows, items=share, reps=3, add=with_add,

@@ -93,3 +93,11 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_extra_entries_parse():
+    assert bench.parse_extra("5") == (5, False, False, False, None)
+    assert bench.parse_extra("5r") == (5, True, False, False, None)
+    assert bench.parse_extra("5a") == (5, False, True, False, None)
+    assert bench.parse_extra("2f") == (2, False, False, True, None)
+    assert bench.parse_extra("5s8") == (5, False, False, False, 8)
