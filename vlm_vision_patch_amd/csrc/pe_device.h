@@ -1,0 +1,85 @@
+// pe_device.h -- device helpers shared by the gfx950 kernels: 16-byte vector types, the raw
+// buffer descriptor word, bf16 rounding, the output stores (with the optional fused addend) and
+// a compile-time loop.
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+#include "pe_internal.h"
+
+namespace pe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// gfx9 buffer descriptor word 3: 32-bit data format, raw (untyped) access.
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+template <int OSZ>
+__device__ __forceinline__ void store_out(void *out, int64_t idx, float v) {
+    if constexpr (OSZ == 2) {
+        static_cast<uint16_t *>(out)[idx] = f32_to_bf16_rne(v);
+    } else {
+        static_cast<float *>(out)[idx] = v;
+    }
+}
+
+// One 16-byte output chunk at element `elem` of out (16/OSZ values, fp32, bias included): with a
+// fused addend (an [N, E] tensor in the output dtype and row order, e.g. the position embeddings
+// that follow PatchEmbed) its chunk at the same position is added in fp32 first; then one
+// round-to-nearest-even cast and a non-temporal store.
+template <int OSZ>
+__device__ __forceinline__ void store_chunk_r(void *out, bool add, const u32x4 &ad, int64_t elem, float (&v)[16 / OSZ]) {
+    if (add) {
+        if constexpr (OSZ == 2) {
+            const uint32_t d[4] = {ad.x, ad.y, ad.z, ad.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] += __builtin_bit_cast(float, d[i] << 16);
+                v[2 * i + 1] += __builtin_bit_cast(float, d[i] & 0xffff0000u);
+            }
+        } else {
+            const f32x4 af = __builtin_bit_cast(f32x4, ad);
+            v[0] += af.x; v[1] += af.y; v[2] += af.z; v[3] += af.w;
+        }
+    }
+    char *dst = static_cast<char *>(out) + elem * OSZ;
+    if constexpr (OSZ == 2) {
+        u32x4 o;
+        o.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        o.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        o.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
+        o.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
+    } else {
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(dst));
+    }
+}
+template <int OSZ>
+__device__ __forceinline__ void store_chunk(void *out, const void *addend, int64_t elem, float (&v)[16 / OSZ]) {
+    u32x4 ad = u32x4{0u, 0u, 0u, 0u};
+    if (addend) ad = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(addend) + elem * OSZ);
+    store_chunk_r<OSZ>(out, addend != nullptr, ad, elem, v);
+}
+
+// Compile-time loop: f(IC<0>{}), f(IC<1>{}), ..., f(IC<N-1>{}).
+template <int N> using IC = std::integral_constant<int, N>;
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(IC<Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+}  // namespace pe

@@ -1,6 +1,6 @@
-// pe_internal.h -- types shared by the C ABI (pe_api.cpp) and the gfx950 kernels
-// (pe_kernels.h and the .hip units that instantiate it). Not installed; the public interface is
-// include/pe.h.
+// pe_internal.h -- types shared by the C ABI (pe_api.cpp) and the gfx950 kernels (pe_device.h,
+// pe_gather.h, the kernel headers and the .hip units that instantiate them). Not installed; the
+// public interface is include/pe.h.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -13,7 +13,7 @@
 // reduction and the variance from a second one over the centred register values (no
 // E[x^2] - mean^2 cancellation), then the row is written back from the registers. Rows are
 // independent and each element is read and written by the same lane, so y may be x.
-#include "pe_kernels.h"
+#include "pe_device.h"
 
 namespace pe {
 
