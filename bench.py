@@ -15,6 +15,7 @@ import hashlib
 import json
 import math
 import os
+import struct
 import sys
 import time
 
@@ -25,13 +26,72 @@ METRIC = "PatchEmbed patches/s + TFLOP/s (% bf16 MFMA peak) on 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_F32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = sorted(glob.glob(os.path.join(ROOT, "vlm_vision_patch_amd", "csrc", "*")))
+LIBPE = os.path.join(ROOT, "vlm_vision_patch_amd", "libpe.so")
 
 
-def kernel_hash() -> str:
+def elf_sections(b):
+    """Section headers of a little-endian ELF64 image: ({name: header}, [headers]); a header is
+    (name, type, flags, addr, offset, size, link, info, align, entsize)."""
+    if b[:4] != b"\x7fELF" or b[4] != 2 or b[5] != 1:
+        raise ValueError("not a little-endian ELF64 image")
+    shoff, = struct.unpack_from("<Q", b, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+    secs = [struct.unpack_from("<IIQQQQIIQQ", b, shoff + i * shentsize) for i in range(shnum)]
+    so = secs[shstrndx][4]
+    return {b[so + s[0]: b.index(b"\0", so + s[0])].decode(): s for s in secs}, secs
+
+
+def gfx950_code_objects(b):
+    """(offset in b, image) of each gfx950 code object of HIP shared library image b: the clang
+    offload bundles (one per translation unit) in its .hip_fatbin section, uncompressed."""
+    named, _ = elf_sections(b)
+    if ".hip_fatbin" not in named:
+        raise ValueError("no .hip_fatbin section")
+    base, size = named[".hip_fatbin"][4], named[".hip_fatbin"][5]
+    fat = b[base: base + size]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    i = fat.find(magic)
+    while i >= 0:
+        n, = struct.unpack_from("<Q", fat, i + len(magic))
+        p = i + len(magic) + 8
+        for _ in range(n):
+            off, size, tl = struct.unpack_from("<QQQ", fat, p)
+            triple = fat[p + 24: p + 24 + tl].decode()
+            p += 24 + tl
+            if triple.endswith("gfx950") and size:
+                yield base + i + off, fat[i + off: i + off + size]
+        i = fat.find(magic, i + len(magic))
+
+
+def kernel_symbols(b, kernel):
+    """(name, offset in b, size) of every symbol of template pe::`kernel` in the gfx950 code of
+    library image b: each instantiation's entry (machine code) and its descriptor (`.kd`:
+    registers, LDS, launch bounds)."""
+    prefix = "_ZN2pe%d%s" % (len(kernel), kernel)
+    for base, co in gfx950_code_objects(b):
+        named, secs = elf_sections(co)
+        st, sn = named[".symtab"], named[".strtab"]
+        for k in range(st[5] // 24):
+            nmo, _info, _other, shndx, val, size = struct.unpack_from("<IBBHQQ", co, st[4] + 24 * k)
+            if size == 0 or shndx == 0 or shndx >= len(secs):
+                continue
+            name = co[sn[4] + nmo: co.index(b"\0", sn[4] + nmo)].decode()
+            if name.startswith(prefix):
+                sec = secs[shndx]
+                yield name, base + sec[4] + val - sec[3], size
+
+
+def kernel_code_hash(kernel: str, lib: str = LIBPE) -> str:
+    """Hash of the machine code of every instantiation of pe::`kernel` in the built library (each
+    symbol's name and bytes, in name order). It keys HBM-traffic counters to the code they were
+    taken on: a change to that kernel's code changes it; a comment or another kernel does not."""
+    b = open(lib, "rb").read()
+    syms = sorted(kernel_symbols(b, kernel))
+    if not syms:
+        raise ValueError("no code for kernel %s in %s" % (kernel, lib))
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+    for name, off, size in syms:
+        h.update(name.encode() + b"\0" + b[off: off + size])
     return h.hexdigest()[:16]
 
 
@@ -152,6 +212,14 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
                 kind=kind, grid=grid, frames=frames)
 
 
+def layernorm_alg_bytes(wl):
+    """Algorithmic HBM bytes of one LayerNorm over the workload's [N, E] output rows: the rows read
+    once and written once, gamma and beta, all in the output dtype."""
+    esz = {"bf16": 2, "f32": 4}[wl.out_dtype]
+    n = sum(t * h * w for (t, h, w) in wl.grid)
+    return 2 * n * wl.embed * esz + 2 * wl.embed * esz
+
+
 def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6, eager=False):
     """The PatchMerger front end on the workload's output rows: pe_layernorm over [N, E] in the
     output dtype (synthetic rows and parameters), alone and after the PatchEmbed as one step
@@ -222,8 +290,7 @@ def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6, eager=False):
         per.sort()
         res[name] = per[len(per) // 2]
     mod.close()
-    esz = rows.element_size()
-    ln_bytes = 2 * n * E * esz + 2 * E * esz
+    ln_bytes = layernorm_alg_bytes(wl)
     ln_ms = res["layernorm"]
     return {"what": "LayerNorm over E of the [N, E] %s rows (the PatchMerger front end; in merge-window "
                     "order the 2x2 concatenation is a view)" % wl.out_dtype,
@@ -379,14 +446,14 @@ def cpu_baseline(r, target_seconds=15.0):
 
 def load_traffic(kernel, workload):
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters, if they were
-    taken on the current kernel sources."""
+    taken on the kernel's current machine code."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
         rec = d.get(workload)
-        if rec and rec.get("kernel_hash") == kernel_hash():
+        if rec and rec.get("code_hash") == kernel_code_hash(kernel):
             return rec["bytes_per_launch"]
     except Exception:
         return None
@@ -414,18 +481,21 @@ def pmc_per_dispatch(csv_dir, counter, kernel):
 def summarize_pmc(workload, kernel, fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes, name=None):
     """HBM bytes per launch of `kernel` on `workload` from two rocprofv3 --pmc runs (FETCH_SIZE, then
     WRITE_SIZE, in KiB per dispatch), each scaled by what the same counter read for one plain device
-    copy of cal_bytes bytes (bench.py --copy-calibrate), into profiles/traffic.json under the current
-    kernel sources hash."""
+    copy of cal_bytes bytes (bench.py --copy-calibrate), into profiles/traffic.json under the hash of
+    the kernel's machine code in the built library."""
     import workloads
     wl = workloads.WORKLOADS[workload]
-    _, _, alg = algorithmic(wl)
+    if kernel == "pe_layernorm_kernel":  # the LayerNorm over the workload's output rows
+        alg, name = layernorm_alg_bytes(wl), name or wl.name + "_layernorm"
+    else:
+        _, _, alg = algorithmic(wl)
     fk, nf = pmc_per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
     wk, nw = pmc_per_dispatch(write_dir, "WRITE_SIZE", kernel)
     cf, _ = pmc_per_dispatch(cal_fetch_dir, "FETCH_SIZE", "copyBuffer")
     cw, _ = pmc_per_dispatch(cal_write_dir, "WRITE_SIZE", "copyBuffer")
     ff, wf = cal_bytes / (cf * 1024.0), cal_bytes / (cw * 1024.0)
     total = fk * 1024.0 * ff + wk * 1024.0 * wf
-    rec = {"kernel_hash": kernel_hash(), "kernel": kernel, "fetch_kib_per_launch": round(fk, 1),
+    rec = {"code_hash": kernel_code_hash(kernel), "kernel": kernel, "fetch_kib_per_launch": round(fk, 1),
            "write_kib_per_launch": round(wk, 1), "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
            "bytes_per_launch": int(round(total)), "algorithmic_bytes_per_launch": alg,
            "launches_counted": min(nf, nw)}

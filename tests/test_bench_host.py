@@ -1,6 +1,7 @@
 """CPU checks of bench.py's host-side arithmetic: the algorithmic FLOPs and bytes of each workload
 (the units behind `roofline.achieved` and `hbm_frac`), the row sample of the CPU baseline and its
-parity check, the counter summary behind `roofline.traffic`, and the refusal of more than one GPU.
+parity check, the counter summary behind `roofline.traffic` and the machine-code hash that keys it,
+and the refusal of more than one GPU.
 The kernel the bench names comes from the library's own launch plan (pe_forward_plan), tested in
 test_plan.py and on the GPU."""
 import os
@@ -66,7 +67,10 @@ def test_cpu_info_states_model_and_share():
 
 
 def test_summarize_pmc_reads_rocprof_csv(tmp_path, monkeypatch):
-    """Per-dispatch sums of a counter's instance rows, averaged over dispatches, scaled by a copy."""
+    """Per-dispatch sums of a counter's instance rows, averaged over dispatches, scaled by a copy;
+    the record is read back for the kernel's current code only."""
+    if not os.path.exists(bench.LIBPE):
+        pytest.skip("libpe.so not built (the record is keyed by the kernel's machine code)")
     hdr = "Correlation_Id,Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
 
     def write(d, rows):
@@ -86,6 +90,11 @@ def test_summarize_pmc_reads_rocprof_csv(tmp_path, monkeypatch):
     # copy of 1 MiB: fetch reads 512 KiB (factor 2), write 1024 KiB (factor 1)
     assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
     assert rec["bytes_per_launch"] == 150 * 1024 * 2 + 200 * 1024
+    name = workloads.WORKLOADS[5].name
+    assert bench.load_traffic("pe_fwd32_kernel", name) == rec["bytes_per_launch"]
+    # counters taken on other code are not used
+    monkeypatch.setattr(bench, "kernel_code_hash", lambda k, lib=None: "0" * 16)
+    assert bench.load_traffic("pe_fwd32_kernel", name) is None
 
 
 def test_more_than_one_gpu_is_refused():
@@ -101,3 +110,34 @@ def test_extra_entries_parse():
     assert bench.parse_extra("5a") == (5, False, True, False, None)
     assert bench.parse_extra("2f") == (2, False, False, True, None)
     assert bench.parse_extra("5s8") == (5, False, False, False, 8)
+
+
+FAMILIES = ("pe_fwd32_kernel", "pe_fwd32_sk_kernel", "pe_fwd16_kernel", "pe_layernorm_kernel")
+
+
+def test_kernel_code_hash_follows_the_code(tmp_path):
+    """The key of the committed traffic counters: one hash per kernel template, from its machine
+    code in libpe.so. A one-byte change inside one instantiation of one kernel changes that
+    kernel's hash and no other."""
+    if not os.path.exists(bench.LIBPE):
+        pytest.skip("libpe.so not built")
+    b = open(bench.LIBPE, "rb").read()
+    hs = {k: bench.kernel_code_hash(k) for k in FAMILIES}
+    assert len(set(hs.values())) == len(FAMILIES)
+    assert hs == {k: bench.kernel_code_hash(k) for k in FAMILIES}
+    with pytest.raises(ValueError):
+        bench.kernel_code_hash("pe_no_such_kernel")
+    # both the entries and their descriptors are found, and the two template names do not overlap
+    syms = list(bench.kernel_symbols(b, "pe_fwd16_kernel"))
+    assert any(n.endswith(".kd") for n, _, _ in syms) and any(not n.endswith(".kd") for n, _, _ in syms)
+    assert not any("sk_kernel" in n for n, _, _ in bench.kernel_symbols(b, "pe_fwd32_kernel"))
+    name, off, size = next((n, o, z) for n, o, z in sorted(syms) if not n.endswith(".kd"))
+    assert size > 64
+    mutated = bytearray(b)
+    mutated[off + size // 2] ^= 0x01
+    lib2 = tmp_path / "libpe.so"
+    lib2.write_bytes(bytes(mutated))
+    after = {k: bench.kernel_code_hash(k, str(lib2)) for k in FAMILIES}
+    assert after["pe_fwd16_kernel"] != hs["pe_fwd16_kernel"]
+    assert {k: v for k, v in after.items() if k != "pe_fwd16_kernel"} == \
+        {k: v for k, v in hs.items() if k != "pe_fwd16_kernel"}
