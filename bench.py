@@ -112,7 +112,7 @@ def algorithmic(wl, rows=False, add=False):
 
 
 def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=10, cold=False, add=False,
-                  fold=False, keep_out=False):
+                  fold=False, keep_out=False, stage=False):
     """rows: feed the workload's patches as pre-flattened rows [N, K] (the processor's
     pixel_values layout) instead of its frames: same N, weight and bias, synthetic N(0, 1) rows.
     items: keep only the first `items` items (one GPU's share of an item split).
@@ -121,6 +121,7 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     Infinity Cache hold nothing of the inputs), median of `reps`.
     add: fuse the add of a synthetic [N, E] tensor (position embeddings) into the epilogue.
     fold: the approximate image-fold mode (single-frame items on W[:, :, 0] + W[:, :, 1] in bf16).
+    stage: the opt-in LDS-staged gather of single images (stage_images).
     keep_out: also return the output of the last timed step (and the inputs, on the host), for the
     parity check of the timed output.
     The result holds the library's launch plan of one step (pe_forward_plan): which kernel runs,
@@ -144,7 +145,8 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     host_in = (x, w, b) if keep_out else None
     x, w = x.to(dev), w.to(dev)
     b = b.to(dev) if b is not None else None
-    mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype], image_fold=fold)
+    mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype], image_fold=fold,
+                        stage_images=stage)
     plan = mod.plan(grid, frames, kind=kind, in_dtype=x.dtype)
     out = torch.empty((n, wl.embed), dtype=workloads.DTYPES[wl.out_dtype], device=dev)
     addend = None
@@ -509,11 +511,12 @@ def summarize_pmc(workload, kernel, fetch_dir, write_dir, cal_fetch_dir, cal_wri
 
 
 def parse_extra(spec):
-    """One --extra entry: (workload, as patch rows, fused add, image fold, items kept or None).
-    '5r' patch rows, '5a' fused add, '5f' fold, '5s8' the first 8 items."""
-    as_rows, with_add, fold = spec.endswith("r"), spec.endswith("a"), spec.endswith("f")
+    """One --extra entry: (workload, as patch rows, fused add, image fold, items kept or None,
+    LDS-staged images). '5r' patch rows, '5a' fused add, '5f' fold, '5s8' the first 8 items, '5l'
+    the opt-in LDS-staged gather."""
+    as_rows, with_add, fold, stage = spec.endswith("r"), spec.endswith("a"), spec.endswith("f"), spec.endswith("l")
     share = int(spec.split("s")[1]) if "s" in spec else None
-    return int(spec.rstrip("raf").split("s")[0]), as_rows, with_add, fold, share
+    return int(spec.rstrip("rafl").split("s")[0]), as_rows, with_add, fold, share, stage
 
 
 def workloads_name(idx):
@@ -529,7 +532,7 @@ def main():
     ap.add_argument("--workload", type=int, default=5,
                     help="the headline workload (default 5: 64 images of 1008 x 1008, 331,776 patches, the "
                          "largest configuration and the one the bf16 matrix-core fraction is quoted on)")
-    ap.add_argument("--extra", type=str, default="2,5r,5a,5n,5f,2f,5s8,3,4,6,1",
+    ap.add_argument("--extra", type=str, default="2,5r,5a,5n,5f,5l,2f,5s8,3,4,6,1",
                     help="comma-separated further workloads reported under 'also' ('' for none); "
                          "a trailing r feeds that workload's patches as pre-flattened rows, a trailing "
                          "a fuses the add of an [N, E] tensor, a trailing n times the PatchMerger "
@@ -610,18 +613,18 @@ def main():
             also[workloads_name(e) + "_merger_layernorm"] = time_merger_front(e, max(5, min(args.steps, 50)),
                                                                                eager=args.eager)
             continue
-        e, as_rows, with_add, fold, share = parse_extra(spec)
-        if e == args.workload and not (as_rows or with_add or fold or share is not None):
+        e, as_rows, with_add, fold, share, stage = parse_extra(spec)
+        if e == args.workload and not (as_rows or with_add or fold or stage or share is not None):
             continue
         st = max(5, min(args.steps, 50))
         q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows, items=share, reps=3, add=with_add,
-                          fold=fold)
+                          fold=fold, stage=stage)
         qt = q["ms"] / 1e3
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
         qai = q["flops"] / q["bytes"]
         qdom = max(q["plan"], key=lambda L: L["n_rows"])
         also[q["wl"].name + ("_as_patch_rows" if as_rows else "") + ("_plus_pos_embed" if with_add else "")
-             + ("_image_fold_approx" if fold else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
+             + ("_image_fold_approx" if fold else "") + ("_lds_staged" if stage else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
                               "tflops": round(q["flops"] / qt / 1e12, 2),
                               "frac_matrix_peak": round(q["flops"] / qt / 1e12 / qpk, 4),
                               "frac_hbm": round(q["bytes"] / qt / 1e9 / PEAK_HBM_GBS, 4),

@@ -67,7 +67,18 @@ typedef struct {
     int32_t out_order;            /* pe_order, applied to FRAMES input.                      */
     int32_t image_fold;           /* 0: exact (default). 1: APPROXIMATE mode for single-frame   */
                                   /* items, see below. Needs a bf16 weight.                   */
+    int32_t stage_images;         /* 0: default. 1: single images gathered through LDS, see   */
+                                  /* below (exact; slower on MI355X, kept for comparison).    */
 } pe_config;
+
+/* stage_images. With stage_images = 1, frames launches whose items are all single images of one
+ * frame size, with bf16 input and weight, P = 14 and the large tiles, stage the tile's pixel rows
+ * through LDS (each wave loads whole pixel rows of 32 patches and the waves share them, as the
+ * LDS-staged A tiles of a classic GEMM) instead of each wave gathering its own patches' pixels
+ * into registers. Same sum in a different k order (fp32 accumulation, so the
+ * last bits may differ). On MI355X it measured 3-20 %
+ * slower than the default, so it is off unless asked for; pe_forward_plan reports such launches
+ * as PE_A_IMAGES_LDS. Other launches are unaffected. */
 
 /* image_fold. An image item repeats its one frame in both temporal slots, so its output is
  * x . (W[:, :, 0] + W[:, :, 1]) over the C*P*P elements of that frame (the per-temporal-slice sum of
@@ -152,7 +163,9 @@ typedef enum {
     PE_A_FRAMES = 0,         /* frames with two temporal slots (videos, or images mixed with videos) */
     PE_A_IMAGES = 1,         /* frames, every item one image frame (both slots the same pixels)    */
     PE_A_PATCH_ROWS = 2,     /* pre-flattened patch rows                                            */
-    PE_A_FOLDED_IMAGES = 3   /* single images against the folded weight (image_fold = 1)            */
+    PE_A_FOLDED_IMAGES = 3,  /* single images against the folded weight (image_fold = 1)            */
+    PE_A_IMAGES_LDS = 4      /* single images, bf16 input, P = 14, large tiles: each wave stages its
+                                patches' pixel rows through LDS (whole-row loads)                 */
 } pe_a_mode;
 
 /* One kernel launch of a pe_forward call, as pe_forward_plan describes it. */

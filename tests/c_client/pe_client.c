@@ -71,7 +71,7 @@ static int run_rows(const char *dir) {
     const size_t K = (size_t)3 * 2 * P * P, isz = in_dtype == PE_BF16 ? 2 : 4;
     if (nx != (size_t)N * K * isz) { fprintf(stderr, "rows.bin holds %zu bytes, not N*K*%zu\n", nx, isz); return 1; }
     void *dx = to_device(x, nx), *dw = to_device(wt, nw), *db = to_device(b, nb);   /* exactly N*K elements */
-    pe_config cfg = {3, 2, P, E, 2, PE_BF16, PE_BF16, PE_ORDER_RASTER, 0};
+    pe_config cfg = {3, 2, P, E, 2, PE_BF16, PE_BF16, PE_ORDER_RASTER, 0, 0};
     pe_handle hd = NULL;
     CHECK(pe_create(&cfg, dw, db, NULL, &hd));
     const int32_t grid[3] = {1, 1, N};
@@ -108,7 +108,7 @@ int main(int argc, char **argv) {
     void *dx = to_device(x, nx), *dw = to_device(wt, nw), *db = to_device(b, nb);
     void *dg = to_device(g, ng), *dbe = to_device(be, nbe);
 
-    pe_config cfg = {3, 2, P, E, 2, PE_BF16, PE_BF16, PE_ORDER_MERGE_WINDOW, 0};
+    pe_config cfg = {3, 2, P, E, 2, PE_BF16, PE_BF16, PE_ORDER_MERGE_WINDOW, 0, 0};
     pe_handle hd = NULL;
     CHECK(pe_create(&cfg, dw, db, NULL, &hd));
     const int32_t grid[3] = {t, h, w};

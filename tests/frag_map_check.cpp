@@ -149,8 +149,85 @@ static int check_rows_loads(int P) {
     return 0;
 }
 
+// The grouped order and the LDS stage of single images (P = 14): ttg_uf is a permutation of the
+// temporal-split fragments; staging every pixel row as sg_row says (half 0: px 0..7 to slot a;
+// half 1: px 6..13 as d0..d3 to the slots of its kind, rows in increasing u) leaves each group's
+// slots holding exactly the grouped fragments' elements (zeros in the tail); and the load/write
+// schedule writes each row at least two k-steps before the first k-step that reads it (that
+// fragment is read one k-step early), into a group buffer only after
+// the last read of the group it held, through a ring of four registers that no row overwrites
+// while it is still to be written.
+static int check_staged() {
+    using namespace pe;
+    const int P = 14, S = tt_steps(P), NF = 2 * S, NU = kC * P;
+    const int ZERO = -2, UNSET = -1;
+    std::vector<int> seen(NF, 0);
+    for (int g = 0; g < NF; ++g) {
+        const int uf = ttg_uf(P, g);
+        if (uf < 0 || uf >= NF || seen[uf]++) { printf("ttg_uf is not a permutation at %d\n", g); return 1; }
+    }
+    for (int g = 0; g < 2 * tt_steps(16); ++g)
+        if (ttg_uf(16, g) != g) { printf("ttg_uf(16) is not the identity\n"); return 1; }
+    // element id of (u, x): u * P + x
+    const int NG = (NU + kSgRows - 1) / kSgRows;
+    std::vector<int> slots(NG * 14 * 8, UNSET);
+    auto put = [&](int G, int slot, int byte, int first_elem_id, int n, bool zero) {
+        if (slot < 0 || slot >= 14 || byte % 4 || byte + 2 * n > 16) { printf("slot write out of range\n"); return false; }
+        for (int i = 0; i < n; ++i) slots[(G * 14 + slot) * 8 + byte / 2 + i] = zero ? ZERO : first_elem_id + i;
+        return true;
+    };
+    for (int u = 0; u < NU; ++u) {
+        const SgRow w = sg_row(u);
+        const int G = u / kSgRows, e = u * P;   // d_k of half 1 = elements (u, 6 + 2k), (u, 7 + 2k)
+        bool ok = put(G, w.slot_a, 0, e + 0, 8, false);
+        if (w.kind == 0) {
+            ok = ok && put(G, w.slot_b, 0, e + 8, 6, false);
+            ok = ok && put(G, w.slot_b, 12, e + 12, 2, false);                 // junk: d3 again
+        } else if (w.kind == 1) {
+            for (int k = 0; k < 3; ++k) ok = ok && put(G, w.slot_b + k, 12, e + 8 + 2 * k, 2, false);
+        } else if (w.kind == 2) {
+            ok = ok && put(G, w.slot_b, 12, e + 8, 2, false);
+            ok = ok && put(G, w.slot_b + 1, 0, e + 10, 4, false);
+            ok = ok && put(G, w.slot_b + 1, 8, 0, 4, true);
+        } else {
+            ok = false;
+        }
+        if (!ok) { printf("staged write of row %d\n", u); return 1; }
+    }
+    std::vector<int> first_read(NU, 1 << 30);
+    for (int g = 0; g < NF; ++g) {
+        const UFrag f = tt_frag(P, ttg_uf(P, g));
+        const int G = g / 14, slot = g % 14;
+        for (int j = 0; j < 8; ++j) {
+            int want;
+            if (f.kind == kUfTail4 && j >= 4) want = ZERO;
+            else if (f.kind == kUfSplit62 && j >= 6) want = f.u2 * P + f.x2 + j - 6;
+            else want = f.u1 * P + f.x1 + j;
+            const int got = slots[(G * 14 + slot) * 8 + j];
+            if (got != want) { printf("staged fragment %d element %d: %d, want %d\n", g, j, got, want); return 1; }
+            if (want >= 0 && g / 2 < first_read[want / P]) first_read[want / P] = g / 2;
+        }
+    }
+    for (int u = kSgRows; u < NU; ++u) {
+        const int G = u / kSgRows, ld = sg_load_step(u), wr = ld + kSgLag;
+        // the kernel reads k-step s's fragment during k-step s - 1, after that step's writes of
+        // the step before: a row must be written at least two k-steps before its first read
+        if (ld < 0 || wr > first_read[u] - 2) { printf("row %d written at step %d, read at %d\n", u, wr, first_read[u]); return 1; }
+        // group G - 2's last fragment is read during k-step 7(G - 2) + 5 (one ahead)
+        if (G >= 2 && wr < kSgSteps * (G - 2) + kSgSteps - 1) { printf("row %d overwrites group %d early\n", u, G - 2); return 1; }
+        for (int v = u + 1; v < NU; ++v)
+            if (v % 4 == u % 4 && sg_load_step(v) <= wr) { printf("rows %d and %d share a register\n", u, v); return 1; }
+        if (u > kSgRows && sg_load_step(u) < sg_load_step(u - 1)) { printf("loads out of order\n"); return 1; }
+    }
+    for (int u = 0; u < kSgRows; ++u)
+        if (first_read[u] < 0) return 1;
+    printf("staged images P14: %d fragments in %d groups, schedule ok\n", NF, NG);
+    return 0;
+}
+
 int main() {
     int bad = 0;
+    bad |= check_staged();
     for (int P : {14, 16}) bad |= check_rows(P);
     for (int P : {14, 16}) bad |= check_rows_loads(P);
     if (pe::rows_steps(14) != 37 || pe::rows_steps(16) != 48) { printf("rows step counts\n"); bad = 1; }

@@ -105,11 +105,12 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_extra_entries_parse():
-    assert bench.parse_extra("5") == (5, False, False, False, None)
-    assert bench.parse_extra("5r") == (5, True, False, False, None)
-    assert bench.parse_extra("5a") == (5, False, True, False, None)
-    assert bench.parse_extra("2f") == (2, False, False, True, None)
-    assert bench.parse_extra("5s8") == (5, False, False, False, 8)
+    assert bench.parse_extra("5") == (5, False, False, False, None, False)
+    assert bench.parse_extra("5r") == (5, True, False, False, None, False)
+    assert bench.parse_extra("5a") == (5, False, True, False, None, False)
+    assert bench.parse_extra("2f") == (2, False, False, True, None, False)
+    assert bench.parse_extra("5s8") == (5, False, False, False, 8, False)
+    assert bench.parse_extra("5l") == (5, False, False, False, None, True)
 
 
 FAMILIES = ("pe_fwd32_kernel", "pe_fwd32_sk_kernel", "pe_fwd16_kernel", "pe_layernorm_kernel")

@@ -707,6 +707,82 @@ def test_integer_frames_exact_merge_order(pe):
 
 
 # ---------------------------------------------------------------------------------------------
+# single images staged through LDS (opt-in stage_images; bf16, P = 14, one frame size, large
+# tiles): each wave loads whole pixel rows of 32 patches, the waves share them through LDS in the
+# grouped k order. Every case checks first which path the plan runs it on.
+# ---------------------------------------------------------------------------------------------
+
+STAGED = {
+    # name: items (h, w) of single images, merge size (0 = raster), E, out dtype, bias, fused add
+    # (frame_sizes_differ: mixed frame sizes keep the register gather)
+    "raster_ragged": ([(58, 142)], 0, 1280, torch.bfloat16, True, False),        # 8236 rows: tail of 44
+    "merge2_ragged": ([(60, 138)], 2, 1280, torch.bfloat16, True, False),
+    "merge4": ([(64, 120)], 4, 1280, torch.bfloat16, False, False),
+    "merge3": ([(63, 126)], 3, 1280, torch.bfloat16, True, False),               # windows straddle waves
+    "tiles_256x128": ([(64, 64)], 2, 1280, torch.bfloat16, True, False),
+    "frame_sizes_differ": ([(40, 60), (36, 72), (50, 50), (2, 2)], 2, 1280, torch.bfloat16, True, False),
+    "f32_out_e1152": ([(60, 140)], 2, 1152, torch.float32, True, False),
+    "fused_add": ([(58, 142)], 2, 1280, torch.bfloat16, True, True),
+    "identical_images": ([(36, 36)] * 9, 2, 1280, torch.bfloat16, True, False),
+}
+
+
+@pytest.mark.parametrize("case", sorted(STAGED))
+def test_staged_images(pe, case):
+    """stage_images = 1 against the oracle, and the same request on the default path."""
+    items, m, E, od, bias, add = STAGED[case]
+    P = 14
+    K = 3 * 2 * P * P
+    xs = [make(3300 + i, (1, 3, h * P, w * P), torch.bfloat16) for i, (h, w) in enumerate(items)]
+    x = torch.cat([a.reshape(-1) for a in xs])
+    w = make(3301, (E, 3, 2, P, P), torch.bfloat16, "uniform", 1 / math.sqrt(K))
+    b = make(3302, (E,), torch.bfloat16, "uniform", 1 / math.sqrt(K)) if bias else None
+    grid = [[1, h, ww] for (h, ww) in items]
+    frames = [1] * len(items)
+    n = sum(h * ww for (h, ww) in items)
+    order = "merge" if m else "raster"
+    addend = make(3303, (n, E), od) if add else None
+    say("staged images %s: %d items, %d rows, m=%d, E=%d, out=%s, add=%s" % (case, len(items), n, m, E, od, add))
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV) if b is not None else None, order=order, out_dtype=od,
+                        spatial_merge_size=m or 2, stage_images=True)
+    plan = mod.plan(grid, frames)
+    want = "images" if case == "frame_sizes_differ" else "images_lds"
+    assert [L["a_mode"] for L in plan] == [want], plan
+    if add:
+        out = mod(x.to(DEV), grid, frames, add=addend.to(DEV))
+    else:
+        out = mod(x.to(DEV), grid, frames)
+    torch.cuda.synchronize()
+    mod.close()
+    ref = oracle.forward(x, w, b, grid=grid, frames=frames, order=order, m=m or 2, addend=addend)
+    check(out.double().cpu().numpy(), ref, od, "staged " + case)
+    # the default path on the same request: the same sums in another k order
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV) if b is not None else None, order=order, out_dtype=od,
+                        spatial_merge_size=m or 2)
+    assert [L["a_mode"] for L in mod.plan(grid, frames)] == ["images"]
+    out2 = mod(x.to(DEV), grid, frames, add=addend.to(DEV)) if add else mod(x.to(DEV), grid, frames)
+    torch.cuda.synchronize()
+    mod.close()
+    check(out2.double().cpu().numpy(), ref, od, "default " + case)
+
+
+def test_staged_images_integer_exact(pe):
+    """Integer pixels and weights: the staged path's sums are exact, so a fragment staged to the
+    wrong slot, or a grouped weight out of step with it, is an exact miss."""
+    P, h, w = 14, 60, 138
+    x = workloads.random_tensor((1, 3, h * P, w * P), seed=3310, dist="int", low=0, high=3).to(torch.bfloat16)
+    wt = workloads.random_tensor((256, 3, 2, P, P), seed=3311, dist="int", low=-2, high=3).to(torch.bfloat16)
+    say("staged images, integer inputs, %d rows" % (h * w))
+    mod = pe.PatchEmbed(wt.to(DEV), None, order="merge", out_dtype=torch.float32, stage_images=True)
+    assert [L["a_mode"] for L in mod.plan([[1, h, w]], [1])] == ["images_lds"]
+    out = mod(x.to(DEV), [[1, h, w]], [1])
+    torch.cuda.synchronize()
+    mod.close()
+    ref = oracle.forward(x, wt, None, grid=[[1, h, w]], frames=[1], order="merge")
+    assert np.array_equal(out.double().cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------------------------
 # empty input and error paths (validated before any launch)
 # ---------------------------------------------------------------------------------------------
 

@@ -5,10 +5,11 @@ the planning rules. No GPU.
 The model restates the rules the planner implements: the grid checks and their error codes; patch
 rows split at one launch's 4 GiB buffer range; frames grouped greedily into launches of at most 64
 items (any number of identical ones), at most 4 GiB of input, and, with the image fold, runs of
-single images kept apart from videos; and the tile choice (fewest rounds x measured round cost:
-256 x 256 ~30, 256 x 128 ~18, split-k ~8; ties to the larger tile). The sanitizers catch what a
-model cannot: reads past the caller's grid and frame arrays, signed overflow in the int64 size
-arithmetic at the int32 limits.
+single images kept apart from videos; the tile choice (fewest rounds x measured round cost:
+256 x 256 ~30, 256 x 128 ~18, split-k ~8; ties to the larger tile); and the LDS-staged image path
+(single images, bf16 input and weight, P = 14, large tiles) with its grouped weight. The sanitizers
+catch what a model cannot: reads past the caller's grid and frame arrays, signed overflow in the
+int64 size arithmetic at the int32 limits.
 """
 import os
 import random
@@ -38,8 +39,8 @@ def driver(tmp_path_factory):
 def run_driver(exe, reqs):
     lines = []
     for r in reqs:
-        head = [r["P"], r["E"], r["m"], r["wesz"], r["iesz"], r["oesz"], r["merge"], r["fold"], r["ncu"], r["kind"],
-                len(r["grid"]), 1 if r["frames"] is not None else 0]
+        head = [r["P"], r["E"], r["m"], r["wesz"], r["iesz"], r["oesz"], r["merge"], r["fold"], r["stage"], r["ncu"],
+                r["kind"], len(r["grid"]), 1 if r["frames"] is not None else 0]
         body = []
         for i, g in enumerate(r["grid"]):
             body += list(g) + ([r["frames"][i]] if r["frames"] is not None else [])
@@ -56,7 +57,7 @@ def run_driver(exe, reqs):
         elif f[0] == "L":
             v = [int(x) for x in f[1:]]
             keys = ("row0 n_rows in_off in_bytes n_items tile bm bn wg tiles_m tiles_n img fold mixg uni colmajor "
-                    "wmap u_rows u_elems plane rstr kind order").split()
+                    "wmap u_rows u_elems plane rstr kind order staged").split()
             cur["launches"].append(dict(zip(keys, v), items=[]))
         elif f[0] == "I":
             cur["launches"][-1]["items"].append(tuple(int(x) for x in f[1:]))
@@ -130,7 +131,7 @@ def model_plan(r):
             nr = min(per, N - s)
             L = dict(row0=s, n_rows=nr, in_off=s * K * iesz, in_bytes=nr * K * iesz, n_items=0, img=0, fold=0, mixg=0,
                      uni=0, colmajor=int(nr * K * iesz < pcols * K * iesz), wmap=1 if r["wesz"] == 2 else 0,
-                     u_rows=0, u_elems=0, plane=2 * P * P, rstr=P, kind=0, order=0, items=[])
+                     u_rows=0, u_elems=0, plane=2 * P * P, rstr=P, kind=0, order=0, staged=0, items=[])
             tiles(L, nr)
             out.append(L)
         return PE_OK, out
@@ -157,15 +158,20 @@ def model_plan(r):
                  u_rows=row0[i0 + 1] - row0[i0], u_elems=elems[i0], plane=grid[i0][1] * P * grid[i0][2] * P,
                  rstr=grid[i0][2] * P, kind=1, order=int(merge), items=items)
         tiles(L, L["n_rows"])
+        # single images, bf16, P = 14, large tiles: pixel rows staged through LDS, grouped weight
+        L["staged"] = int(bool(r["stage"]) and bool(imgs) and not fold and not mixed and P == 14 and r["wesz"] == 2
+                          and iesz == 2 and L["tile"] in (0, 1))
+        if L["staged"]:
+            L["wmap"] = 3
         out.append(L)
         x0 += span
         i0 = i1
     return PE_OK, out
 
 
-def req(grid, frames=None, P=14, E=1280, m=2, wesz=2, iesz=2, oesz=2, merge=1, fold=0, ncu=256, kind=1):
+def req(grid, frames=None, P=14, E=1280, m=2, wesz=2, iesz=2, oesz=2, merge=1, fold=0, ncu=256, kind=1, stage=0):
     return dict(grid=[tuple(g) for g in grid], frames=frames, P=P, E=E, m=m, wesz=wesz, iesz=iesz, oesz=oesz,
-                merge=merge, fold=fold, ncu=ncu, kind=kind)
+                merge=merge, fold=fold, ncu=ncu, kind=kind, stage=stage)
 
 
 def compare(got, want, r):
@@ -216,6 +222,13 @@ def edge_requests():
     for ncu in (0, 80, 304):
         rs.append(req([[1, 72, 72]] * 64, [1] * 64, ncu=ncu))
         rs.append(req([[1, 16, 64]], [1], ncu=ncu))
+    # the opt-in LDS-staged images: both large tiles, and the launches it leaves alone (split-k,
+    # P = 16, fp32 input, mixed frame sizes, videos, the fold)
+    for g, f, kw in (([[1, 72, 72]] * 64, [1] * 64, {}), ([[1, 64, 64]], [1], {}), ([[1, 16, 64]], [1], {}),
+                     ([[1, 64, 64]], [1], {"P": 16}), ([[1, 64, 64]], [1], {"iesz": 4}),
+                     ([[1, 64, 64], [1, 60, 70]], [1, 1], {}), ([[2, 64, 64]], [4], {}),
+                     ([[1, 72, 72]] * 64, [1] * 64, {"fold": 1}), ([[1, 64, 64]], [1], {"merge": 0})):
+        rs.append(req(g, f, stage=1, **kw))
     return rs
 
 
@@ -231,6 +244,7 @@ def random_requests(seed, count):
         m = rng.choice([1, 2, 2, 3])
         merge = rng.choice([0, 1])
         fold = rng.choice([0, 1]) if wesz == 2 else 0
+        stage = rng.choice([0, 1])
         ncu = rng.choice([0, 256, 256, 80, 304])
         n = rng.choice([1, 2, 3, 5, 17, 64, 65, 130, rng.randint(1, 300)])
         grid, frames = [], []
@@ -255,7 +269,7 @@ def random_requests(seed, count):
             frames.append(f)
         use_frames = kind == 1 and rng.random() < 0.8
         rs.append(req(grid, frames if use_frames else None, P=P, E=E, m=m, wesz=wesz, iesz=iesz, oesz=rng.choice([2, 4]),
-                      merge=merge, fold=fold, ncu=ncu, kind=kind))
+                      merge=merge, fold=fold, ncu=ncu, kind=kind, stage=stage))
     return rs
 
 
@@ -268,7 +282,8 @@ def test_plan_edge_cases_match_model(driver):
 def test_plan_known_answers(driver):
     """Facts the GPU tests and the bench also rely on, written out by hand."""
     rs = [req([[1, 72, 72]] * 64, [1] * 64), req([[1, 16, 64]], [1]), req([[1, 72, 72]] * 720, [1] * 720),
-          req([[1, 1, 1900000]], None, kind=0, merge=0), req([[8, 32, 32]], [16])]
+          req([[1, 1, 1900000]], None, kind=0, merge=0), req([[8, 32, 32]], [16]),
+          req([[1, 72, 72]] * 64, [1] * 64, stage=1)]
     got = run_driver(driver, rs)
     w5 = got[0]["launches"]
     assert len(w5) == 1 and (w5[0]["bm"], w5[0]["bn"], w5[0]["wg"]) == (256, 256, 1296 * 5)
@@ -280,6 +295,11 @@ def test_plan_known_answers(driver):
     rows = got[3]["launches"]
     assert [L["n_rows"] for L in rows] == [1826091, 1900000 - 1826091]
     assert got[4]["launches"][0]["wg"] == 32 * 5 and got[4]["launches"][0]["img"] == 0
+    # the default gathers in registers from the temporal-split weight; stage_images switches the
+    # batch to the LDS-staged kernel and the grouped weight, same tiles
+    assert (w5[0]["staged"], w5[0]["wmap"]) == (0, 0)
+    st = got[5]["launches"]
+    assert len(st) == 1 and (st[0]["staged"], st[0]["wmap"], st[0]["wg"]) == (1, 3, 1296 * 5)
 
 
 @pytest.mark.parametrize("seed", [1, 2, 3])

@@ -24,7 +24,7 @@ PE_INPUT_PATCHES, PE_INPUT_FRAMES = 0, 1
 # every symbol include/pe.h declares
 EXPORTS = ("pe_create", "pe_forward", "pe_forward_add", "pe_forward_plan", "pe_layernorm", "pe_num_rows",
            "pe_destroy", "pe_last_error")
-PE_A_MODES = ("frames", "images", "patch_rows", "folded_images")
+PE_A_MODES = ("frames", "images", "patch_rows", "folded_images", "images_lds")
 
 
 class PEError(RuntimeError):
@@ -37,7 +37,8 @@ class pe_config(ctypes.Structure):
     _fields_ = [("in_channels", ctypes.c_int32), ("temporal_patch_size", ctypes.c_int32),
                 ("patch_size", ctypes.c_int32), ("embed_dim", ctypes.c_int32),
                 ("spatial_merge_size", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("out_order", ctypes.c_int32), ("image_fold", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("out_order", ctypes.c_int32), ("image_fold", ctypes.c_int32),
+                ("stage_images", ctypes.c_int32)]
 
 
 class pe_launch_info(ctypes.Structure):
@@ -181,10 +182,12 @@ class PatchEmbed:
     order   "merge" (2x2 merge-window rows) or "raster" (Conv3d view order) for frames input
     image_fold  approximate mode for single-frame items: W[:, :, 0] + W[:, :, 1] folded into one
             bf16 weight, half the matrix work (see pe.h); off by default
+    stage_images  gather single images through LDS (exact; slower on MI355X, see pe.h); off by
+            default
     """
 
     def __init__(self, weight, bias=None, *, order: str = "raster", out_dtype=None,
-                 spatial_merge_size: int = 2, image_fold: bool = False):
+                 spatial_merge_size: int = 2, image_fold: bool = False, stage_images: bool = False):
         import torch
         if weight.dim() != 5 or weight.shape[3] != weight.shape[4]:
             raise PEError(PE_ERR_INVALID_ARG, "weight must be [E, C, Tp, P, P]")
@@ -199,7 +202,8 @@ class PatchEmbed:
         self.order = order
         cfg = pe_config(int(C), int(Tp), int(P), int(E), int(spatial_merge_size),
                         _dtype_code(weight.dtype), _dtype_code(self.out_dtype),
-                        PE_ORDER_MERGE_WINDOW if order == "merge" else PE_ORDER_RASTER, 1 if image_fold else 0)
+                        PE_ORDER_MERGE_WINDOW if order == "merge" else PE_ORDER_RASTER, 1 if image_fold else 0,
+                        1 if stage_images else 0)
         w = weight.contiguous()
         b = bias.contiguous() if bias is not None else None
         if b is not None and (b.dtype != weight.dtype or b.numel() != E):

@@ -24,6 +24,8 @@ struct pe_handle_s {
     void *wpk;      // packed weight for frames, steps * packed_cols(E) * 64 bytes
     void *wpk_rows; // bf16: the same weight packed for patch rows (inside wpk's allocation); fp32: wpk
     void *wpk_fold; // bf16 with image_fold: W[:, :, 0] + W[:, :, 1] in the fold map (inside wpk's allocation)
+    void *wpk_grp;  // bf16, P = 14 with stage_images: the frames pack in the grouped order, for
+                    // single images staged through LDS (inside wpk's allocation)
     float *bias32;  // fp32 bias or null
 };
 
@@ -114,6 +116,8 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
         return fail(PE_ERR_INVALID_ARG, "image_fold must be 0 or 1 (got %d)", cfg->image_fold);
     if (cfg->image_fold && cfg->weight_dtype != PE_BF16)
         return fail(PE_ERR_UNSUPPORTED, "image_fold needs a bf16 weight");
+    if (cfg->stage_images != 0 && cfg->stage_images != 1)
+        return fail(PE_ERR_INVALID_ARG, "stage_images must be 0 or 1 (got %d)", cfg->stage_images);
 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -126,7 +130,9 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     const size_t rows_bytes = wes == 2 ? (size_t)pe::rows_steps(cfg->patch_size) * pe::packed_cols(cfg->embed_dim, wes) * 64 : 0;
     // and, with image_fold, a third in the folded map for single-frame items
     const size_t fold_bytes = cfg->image_fold ? (size_t)pe::fold_steps(cfg->patch_size) * pe::packed_cols(cfg->embed_dim, wes) * 64 : 0;
-    const size_t wpk_bytes = frames_bytes + rows_bytes + fold_bytes;
+    // and, with stage_images and P = 14, the frames pack again in the grouped order
+    const size_t grp_bytes = (cfg->stage_images && wes == 2 && cfg->patch_size == 14) ? frames_bytes : 0;
+    const size_t wpk_bytes = frames_bytes + rows_bytes + fold_bytes + grp_bytes;
 
     pe_handle h = new (std::nothrow) pe_handle_s;
     if (!h) return fail(PE_ERR_OOM, "host allocation failed");
@@ -141,6 +147,7 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     h->wpk = nullptr;
     h->wpk_rows = nullptr;
     h->wpk_fold = nullptr;
+    h->wpk_grp = nullptr;
     h->bias32 = nullptr;
     e = hipMalloc(&h->wpk, wpk_bytes);
     if (e != hipSuccess) {
@@ -150,6 +157,7 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
     }
     h->wpk_rows = rows_bytes ? static_cast<char *>(h->wpk) + frames_bytes : h->wpk;
     h->wpk_fold = fold_bytes ? static_cast<char *>(h->wpk) + frames_bytes + rows_bytes : nullptr;
+    h->wpk_grp = grp_bytes ? static_cast<char *>(h->wpk) + frames_bytes + rows_bytes + fold_bytes : nullptr;
     if (bias) {
         e = hipMalloc(reinterpret_cast<void **>(&h->bias32), sizeof(float) * cfg->embed_dim);
         if (e != hipSuccess) {
@@ -164,6 +172,8 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
         e = pe::launch_pack(weight, wes, h->wpk_rows, cfg->patch_size, cfg->embed_dim, pe::kPackRows, st);
     if (e == hipSuccess && fold_bytes)
         e = pe::launch_pack(weight, wes, h->wpk_fold, cfg->patch_size, cfg->embed_dim, pe::kPackFold, st);
+    if (e == hipSuccess && grp_bytes)
+        e = pe::launch_pack(weight, wes, h->wpk_grp, cfg->patch_size, cfg->embed_dim, pe::kPackTTG, st);
     if (e == hipSuccess && bias) e = pe::launch_bias(bias, wes, h->bias32, cfg->embed_dim, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) {
@@ -204,6 +214,7 @@ void fill_request(pe_handle h, int32_t input_kind, int32_t in_dtype, const int32
     rq.out_esz = esize(cfg.out_dtype);
     rq.merge = cfg.out_order == PE_ORDER_MERGE_WINDOW;
     rq.image_fold = cfg.image_fold;
+    rq.stage_images = cfg.stage_images;
     rq.num_cus = h->num_cus;
     rq.input_kind = input_kind;
     rq.grid_thw = grid_thw;
@@ -255,7 +266,13 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
     const int64_t row_bytes = (int64_t)cfg.embed_dim * rq.out_esz;
     for (pe::Launch &L : plan) {
         pe::FwdArgs &a = L.a;
-        a.wpk = L.weight_map == pe::kWeightRows ? h->wpk_rows : (L.weight_map == pe::kWeightFold ? h->wpk_fold : h->wpk);
+        switch (L.weight_map) {
+            case pe::kWeightRows: a.wpk = h->wpk_rows; break;
+            case pe::kWeightFold: a.wpk = h->wpk_fold; break;
+            case pe::kWeightGrouped: a.wpk = h->wpk_grp; break;
+            default: a.wpk = h->wpk; break;
+        }
+        if (!a.wpk) return fail(PE_ERR_UNSUPPORTED, "the plan asks for a packed weight the handle does not hold");
         a.bias = h->bias32;
         a.in = static_cast<const char *>(input) + L.in_off;
         a.out = static_cast<char *>(out) + L.row0 * row_bytes;
@@ -309,7 +326,11 @@ int pe_forward_plan(pe_handle h, int32_t input_kind, int32_t in_dtype, const int
         o.in_offset = (int64_t)L.in_off;
         o.in_bytes = L.a.in_bytes;
         o.n_items = L.a.n_items;
-        o.a_mode = L.a.kind == 0 ? PE_A_PATCH_ROWS : (L.a.fold ? PE_A_FOLDED_IMAGES : (L.a.img ? PE_A_IMAGES : PE_A_FRAMES));
+        o.a_mode = L.a.kind == 0 ? PE_A_PATCH_ROWS
+                 : L.a.fold      ? PE_A_FOLDED_IMAGES
+                 : L.a.staged    ? PE_A_IMAGES_LDS
+                 : L.a.img       ? PE_A_IMAGES
+                                 : PE_A_FRAMES;
     }
     return plan.size() > (size_t)INT32_MAX ? fail(PE_ERR_SHAPE, "too many launches") : (int)plan.size();
 }

@@ -34,7 +34,23 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     constexpr int AL = BM * 8 / NT;                // 16-byte A loads per thread per piece
     static_assert(!AST || (BM * 8) % NT == 0, "A piece loads");
     constexpr int AOFF = 2 * KBUF;                 // A stages after the weight buffers
-    constexpr int MAIN_BYTES = 2 * KBUF + (AST ? 2 * ASTAGE : 0);
+    // Single images, P = 14 (AM == kAStaged): the tile's pixel rows are staged through LDS in the
+    // grouped fragment order (pe_internal.h), 8 pixel rows (7 k-steps) per group, two group
+    // buffers of BM patches. Wave w stages the 32-row slice w of the tile: a pixel row of its 32
+    // patches is one load instruction, 16 bytes per lane, the 28 bytes of each patch in two lanes,
+    // so the wave's bytes are contiguous runs of the image row (whole cache lines) instead of 16
+    // bytes at a 28-byte stride per fragment. Shared A lets a wave take 64 rows (TM = 2) and half
+    // the weight fragments per product. A row is written at least two k-steps before the first
+    // read of it (the per-step barrier in between publishes it) and into a group buffer only
+    // after the last read of the group it held. Patch pitch 240 bytes (14 fragments + 16): the 16
+    // lanes of a 16-byte read land on distinct banks.
+    constexpr bool SG = AM == kAStaged;
+    static_assert(!SG || (P == 14 && ISZ == 2 && S == 37 && BM == 32 * WM * WN && KS == 1),
+                  "LDS-staged images: bf16, P = 14, one 32-row slice per wave, a barrier per k-step");
+    constexpr int SG_PITCH = 240;
+    constexpr int SG_BLOCK = BM * SG_PITCH;        // one group of the tile's patches
+    constexpr int SGOFF = 2 * KBUF;                // after the weight buffers
+    constexpr int MAIN_BYTES = 2 * KBUF + (AST ? 2 * ASTAGE : 0) + (SG ? 2 * SG_BLOCK : 0);
     constexpr int LDS_BYTES = (MAIN_BYTES > EP_WAVE * WM * WN) ? MAIN_BYTES : EP_WAVE * WM * WN;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
@@ -138,6 +154,63 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
             }
     };
 
+    // LDS-staged images: pixel row u of the lane's patch in the wave's slice (part 0: px 0..7,
+    // part 1: px 6..13); the per-row part of the address is a scalar for one frame geometry, per lane
+    // otherwise. Every byte read lies inside the patch's own pixel row (tail rows past the launch
+    // read patch 0).
+    // Loading lane L takes part L & 1 of patch L >> 1 of the slice: a quad of lanes reads two
+    // neighbouring patches' 56 contiguous bytes, and the two half-waves read different patches
+    // (were they to read the same cache lines, the loads would take about twice the time in the
+    // texture data path).
+    const int sgp = lane >> 1, sgh = lane & 1;
+    uint32_t sgv = 0u, sgpl = 0u, sgrs = 0u;
+    auto sg_setup = [&]() {
+        const PatchRef p = patch_of_row<P>(a, row0 + wave * 32 + sgp);
+        sgv = p.base * 2u + (sgh ? 12u : 0u);
+        sgpl = p.plane;
+        sgrs = p.rstr;
+    };
+    auto sg_load = [&](auto uc) -> u32x4 {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (MG)
+            return __builtin_amdgcn_raw_buffer_load_b128(
+                rsrc, (int)(sgv + ((uint32_t)(u / P) * sgpl + (uint32_t)(u % P) * sgrs) * 2u), 0, 0);
+        else
+            return __builtin_amdgcn_raw_buffer_load_b128(
+                rsrc, (int)sgv, (int)(((uint32_t)(u / P) * plane + (uint32_t)(u % P) * rstr) * 2u), 0);
+    };
+    // ... and its place in the group buffer (sg_row): the lane's patch slot
+    const uint32_t sgw = SGOFF + (uint32_t)(wave * 32 + sgp) * SG_PITCH;
+    auto sg_write = [&](auto uc, const u32x4 &v) {
+        constexpr int u = decltype(uc)::value;
+        constexpr SgRow w = sg_row(u);
+        unsigned char *gb = lds + sgw + ((u / kSgRows) & 1) * SG_BLOCK;
+        const bool h = sgh;   // the part this lane loaded
+        if constexpr (w.kind == 0) {
+            *reinterpret_cast<u32x4 *>(gb + (h ? 16 * w.slot_b : 16 * w.slot_a)) = h ? u32x4{v.y, v.z, v.w, v.w} : v;
+        } else if constexpr (w.kind == 1) {
+            // four dword writes in every lane (no branch): part 0 its 16 bytes at slot a, part 1
+            // d1..d3 at byte 12 of slots b..b+2 and d3 there once more
+            *reinterpret_cast<uint32_t *>(gb + (h ? 16 * w.slot_b + 12 : 16 * w.slot_a)) = h ? v.y : v.x;
+            *reinterpret_cast<uint32_t *>(gb + (h ? 16 * (w.slot_b + 1) + 12 : 16 * w.slot_a + 4)) = h ? v.z : v.y;
+            *reinterpret_cast<uint32_t *>(gb + (h ? 16 * (w.slot_b + 2) + 12 : 16 * w.slot_a + 8)) = h ? v.w : v.z;
+            *reinterpret_cast<uint32_t *>(gb + (h ? 16 * (w.slot_b + 2) + 12 : 16 * w.slot_a + 12)) = v.w;
+        } else {
+            *reinterpret_cast<u32x4 *>(gb + (h ? 16 * (w.slot_b + 1) : 16 * w.slot_a)) = h ? u32x4{v.z, v.w, 0u, 0u} : v;
+            // part 1: d1 at byte 12 of slot b; part 0 rewrites its own last dword
+            *reinterpret_cast<uint32_t *>(gb + (h ? 16 * w.slot_b + 12 : 16 * w.slot_a + 12)) = h ? v.y : v.w;
+        }
+    };
+    // grouped fragment 2s + h of the lane's row in 32-row block rb of the wave; each k-step reads
+    // the next one's (sg_next)
+    const uint32_t sgr = SGOFF + (uint32_t)(wm * TM * 32 + l32) * SG_PITCH + (h ? 16u : 0u);
+    u32x4 sg_next[TM];
+    auto sg_read = [&](int s, int rb) -> u32x4 {
+        const int g = s / kSgSteps;
+        return *reinterpret_cast<const u32x4 *>(lds + sgr + (g & 1) * SG_BLOCK + rb * 32 * SG_PITCH +
+                                                (2 * s - 2 * kSgSteps * g) * 16);
+    };
+
     // Packed weight of k-step s for the tile's columns: BN*64 contiguous bytes. Chunks past the
     // last column block get an offset beyond the buffer range and read 0 (no branches: branches
     // would make the wait counts conservative).
@@ -180,7 +253,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         constexpr int s = decltype(sc)::value;
         AFrag<ISZ> ald_lds[TM][2];
         if constexpr (AST) read_a(s, ald_lds);
-        const AFrag<ISZ>(&ald)[TM][2] = AST ? ald_lds : ald_regs;
+        if constexpr (SG)
+#pragma unroll
+            for (int rb = 0; rb < TM; ++rb) ald_lds[rb][0].d[0] = sg_next[rb];   // read during the previous k-step
+        const AFrag<ISZ>(&ald)[TM][2] = (AST || SG) ? ald_lds : ald_regs;
         u32x4 af[TM][2];
         a_operands<P, TM, AM, ISZ, s>(ald, af, h);
         // fragment (j, cb) of this step: 1 KB at stage + (wn*TN + cb)*2 KB + j*1 KB
@@ -202,6 +278,11 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
             for (int rb = 0; rb < TM; ++rb)
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, af[rb][j]), __builtin_bit_cast(bf16x8, bf), acc[rb][cb], 0, 0, 0);
+            // staged images: the next k-step's fragment, half-way through this one's products
+            if constexpr (SG && s + 1 < S)
+                if (f == NF / 2 - 1)
+#pragma unroll
+                    for (int rb = 0; rb < TM; ++rb) sg_next[rb] = sg_read(s + 1, rb);
         }
         // Pin the interleave: PF fragment reads first, then per fragment its TM products and the
         // read PF fragments ahead (left alone, the scheduler sinks each read next to its use).
@@ -210,6 +291,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         for (int f = 0; f < NF; ++f) {
             __builtin_amdgcn_sched_group_barrier(0x008, TM, 0);
             if (f + PF < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (SG && s + 1 < S && f == NF / 2 - 1) __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);
         }
     };
 
@@ -222,11 +304,24 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     // Patch rows: A piece c (k-steps AC*c ..) is loaded at k-step AC*c - 3 and stored into stage
     // c & 1 at the end of k-step AC*c - 1 (its barrier publishes it); at most three pieces are in
     // registers at once.
-    constexpr int RD = AST ? 1 : AD + 1;                 // A ring depth (frames)
-    constexpr int PRE = AST ? 0 : AD;                    // A k-steps loaded before the loop (frames)
+    // LDS-staged images: rows 0..7 are staged before the loop; row u >= 8 is loaded at k-step
+    // sg_load_step(u) into a ring of four and written kSgLag k-steps later (pe_internal.h; rows
+    // are written before the k-step that first reads them, and into a group buffer only after
+    // the reads of the group it held).
+    constexpr int RD = (AST || SG) ? 1 : AD + 1;         // A ring depth (frames)
+    constexpr int PRE = (AST || SG) ? 0 : AD;            // A k-steps loaded before the loop (frames)
+    constexpr int NU = kC * P;                           // pixel rows of one frame's patch
     AFrag<ISZ> Ar[RD][TM][2];
     u32x4 Apc[AST ? 3 : 1][AST ? AL : 1];
+    u32x4 Sr[SG ? 4 : 1];
     u32x4 Br[BD][CH];
+    // staged images: rows 0..7 are loaded with the first weight k-step and written after it is
+    // issued, so the tile's start waits for one round trip to memory, not two
+    u32x4 first[SG ? kSgRows : 1];
+    if constexpr (SG) {
+        sg_setup();
+        static_for<kSgRows>([&](auto uc) { first[decltype(uc)::value] = sg_load(uc); });
+    }
     if constexpr (AST) {
         load_piece(IC<0>{}, Apc[0]);
         store_piece(0, Apc[0]);
@@ -240,7 +335,9 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 #pragma unroll
         for (int j = 0; j < (KS < S ? KS : S); ++j) {
             load_b(j, tmp);
-            if (j == 0 && !AST) rows_setup();
+            if (j == 0 && !AST && !SG) rows_setup();
+            if constexpr (SG)
+                if (j == 0) static_for<kSgRows>([&](auto uc) { sg_write(uc, first[decltype(uc)::value]); });
             store_b(j, tmp);
         }
     }
@@ -250,11 +347,19 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     });
     static_for<(PRE < S ? PRE : S)>([&](auto jc) { load_a(jc, Ar[decltype(jc)::value]); });
     __syncthreads();
+    if constexpr (SG)
+#pragma unroll
+        for (int rb = 0; rb < TM; ++rb) sg_next[rb] = sg_read(0, rb);
     static_for<S>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         constexpr int t = s + KS;
         if constexpr (t + BD - 1 < S) load_b(t + BD - 1, Br[(t + BD - 1) % BD]);
-        if constexpr (AST) {
+        if constexpr (SG) {
+            static_for<NU>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                if constexpr (u >= kSgRows && sg_load_step(u) == s) Sr[u % 4] = sg_load(uc);
+            });
+        } else if constexpr (AST) {
             // piece c with AC*c - 3 == s
             if constexpr ((s + 3) % AC == 0 && (s + 3) / AC < NCH && (s + 3) / AC >= 1)
                 load_piece(IC<(s + 3) / AC>{}, Apc[((s + 3) / AC) % 3]);
@@ -263,6 +368,12 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         }
         compute(sc, Ar[s % RD]);
         if constexpr (t < S) store_b(t, Br[t % BD]);
+        if constexpr (SG) {
+            static_for<NU>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                if constexpr (u >= kSgRows && sg_load_step(u) + kSgLag == s) sg_write(uc, Sr[u % 4]);
+            });
+        }
         if constexpr (AST) {
             // piece c with AC*c - 1 == s
             if constexpr ((s + 1) % AC == 0 && (s + 1) / AC < NCH) store_piece((s + 1) / AC, Apc[((s + 1) / AC) % 3]);

@@ -266,8 +266,9 @@ __device__ __forceinline__ void load_a_step(__amdgpu_buffer_rsrc_t rsrc, const u
     }
 }
 // The matrix-core operands of k-step s from what load_a_step loaded (rounded to bf16 here, where
-// they are used, so a load's wait is not pulled forward): for a paired image step, (lanes 0-31 of
-// x, twice) and (lanes 32-63 of x, twice); otherwise the loads as they are.
+// they are used, so a load's wait is not pulled forward): for a paired image step, or a staged
+// image step (lane half h read grouped fragment 2s + h from LDS), (lanes 0-31 of x, twice) and
+// (lanes 32-63 of x, twice); otherwise the loads as they are.
 __device__ __forceinline__ void swap_halves(const u32x4 &x, u32x4 &lo, u32x4 &hi) {
     const auto r0 = __builtin_amdgcn_permlane32_swap(x.x, x.x, false, false);
     const auto r1 = __builtin_amdgcn_permlane32_swap(x.y, x.y, false, false);
@@ -280,7 +281,7 @@ template <int P, int TM, int AM, int ISZ, int s>
 __device__ __forceinline__ void a_operands(const AFrag<ISZ> (&src)[TM][2], u32x4 (&dst)[TM][2], int h) {
 #pragma unroll
     for (int rb = 0; rb < TM; ++rb) {
-        if constexpr (AM == kAImage && img_paired<P, s>()) {
+        if constexpr ((AM == kAImage && img_paired<P, s>()) || AM == kAStaged) {
             swap_halves(frag_bf16<ISZ>(src[rb][0]), dst[rb][0], dst[rb][1]);
         } else {
             dst[rb][0] = frag_bf16<ISZ>(src[rb][0]);

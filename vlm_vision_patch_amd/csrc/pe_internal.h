@@ -127,6 +127,43 @@ __host__ __device__ constexpr UFrag tt_frag(int P, int uf) {
     return f;
 }
 
+// Grouped order of the same unique fragments, for single images staged through LDS (P = 14): the
+// fragments of each 4 pixel rows a..d = 4q..4q+3 are consecutive, ufg = 7q + k:
+//   k = 0..3: row 4q+k px 0..7 (tt uf 4q+k);  k = 4..6: the split fragment of row 4q+k-4 (tt uf
+//   42 + 3q + k-4);  then ufg 70, 71 = rows 40, 41 px 0..7 and ufg 72, 73 = tt uf 72, 73.
+// So 8 pixel rows fill 14 fragments (7 k-steps) and a group of 8 rows can be staged, used and
+// replaced while the next is loaded. P % 8 == 0 keeps the temporal-split order.
+__host__ __device__ constexpr int ttg_uf(int P, int ufg) {
+    if (P % 8 == 0 || ufg >= 72) return ufg;
+    if (ufg >= 70) return ufg - 30;
+    return ufg % 7 < 4 ? 4 * (ufg / 7) + ufg % 7 : 42 + 3 * (ufg / 7) + ufg % 7 - 4;
+}
+// LDS stage of the grouped order (P = 14): group G = u / 8 of pixel rows u, its fragments
+// ufg = 14G + slot. A lane loads 16 bytes of one pixel row of a patch: part 0 px 0..7 (dwords
+// d0..d3), part 1 px 6..13 (d1..d3 = px 8..13; px 6..7 again, so no load leaves the patch's 28
+// bytes). Where they go, as 16-byte slots of the patch's group:
+//   kind 0: part 0 -> slot a; part 1 -> (d1, d2, d3, junk) at slot b (the junk dword is
+//           overwritten by the later row that owns it)
+//   kind 1: part 0 -> slot a; part 1 -> d1, d2, d3 at byte 12 of slots b, b+1, b+2 (row d)
+//   kind 2: part 0 -> slot a; part 1 -> d1 at byte 12 of slot b, (d2, d3, 0, 0) at slot b+1
+// Rows are written in increasing u.
+struct SgRow { int kind, slot_a, slot_b; };
+__host__ __device__ constexpr SgRow sg_row(int u) {
+    if (u == 40) return SgRow{0, 0, 2};
+    if (u == 41) return SgRow{2, 1, 2};
+    const int b = (u / 4) % 2, i = u % 4;
+    return i < 3 ? SgRow{0, 7 * b + i, 7 * b + 4 + i} : SgRow{1, 7 * b + 3, 7 * b + 4};
+}
+constexpr int kSgRows = 8;   // pixel rows per group
+constexpr int kSgSteps = 7;  // k-steps per group
+// k-step during which pixel row u (u >= 8) is loaded: the rows of group G over the k-steps of
+// group G - 1, two at its first step; each is written to LDS kSgLag steps later (after that
+// step's products). Rows 0..7 are loaded and written before the k loop.
+constexpr int kSgLag = 2;
+__host__ __device__ constexpr int sg_load_step(int u) {
+    return kSgSteps * (u / kSgRows - 1) + (u % kSgRows == 0 ? 0 : u % kSgRows - 1);
+}
+
 // bf16 patch-rows map: a patch row is stored in (c, t, py, px) order, so k-step s and lane
 // group g take its elements [32s + 8g, 32s + 8g + 8): every load is 16 contiguous bytes and a
 // k-step reads 64 contiguous bytes of each row. Elements at K and beyond are zero in the packed
@@ -174,11 +211,12 @@ __host__ __device__ constexpr int packed_steps(int P, int esz) {
 }
 
 // How the bf16 kernels read A: frames with two temporal slots, frames that are all single images
-// (both slots the same pixels), pre-flattened patch rows (the rows map above), or single images
-// against the folded weight (the fold map above).
-enum AMode { kAFrames = 0, kAImage = 1, kARows = 2, kAFold = 3 };
-// packed weight maps
-enum PackMap { kPackTT = 0, kPackRows = 1, kPackFold = 2 };
+// (both slots the same pixels), pre-flattened patch rows (the rows map above), single images
+// against the folded weight (the fold map above), or single images whose pixel rows are staged
+// through LDS in the grouped order (P = 14, bf16 input, large tiles).
+enum AMode { kAFrames = 0, kAImage = 1, kARows = 2, kAFold = 3, kAStaged = 4 };
+// packed weight maps (kPackTTG: the temporal-split map in the grouped order)
+enum PackMap { kPackTT = 0, kPackRows = 1, kPackFold = 2, kPackTTG = 3 };
 
 // Launchers (pe_pack.hip and pe_fwd_p*.hip). Return the launch status.
 // map: PackMap (kPackRows and kPackFold are bf16 only)

@@ -56,6 +56,7 @@ template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int P
 inline hipError_t launch16(const FwdArgs &a, hipStream_t st) {
     constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
     if (a.tiles_m != (a.n_rows + BM - 1) / BM || a.tiles_n != (a.E + BN - 1) / BN) return hipErrorInvalidValue;
+    if (a.staged) return hipErrorInvalidValue;
     hipLaunchKernelGGL((pe_fwd16_kernel<P, ESZ, OSZ, TM, TN, WM, WN, KS, PF, AD>), dim3(a.tiles_m * a.tiles_n),
                        dim3(WM * WN * 64), 0, st, a);
     return hipGetLastError();
@@ -66,6 +67,7 @@ inline hipError_t launch32(const FwdArgs &a, hipStream_t st) {
     constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
     if (a.tiles_m != (a.n_rows + BM - 1) / BM || a.tiles_n != (a.E + BN - 1) / BN) return hipErrorInvalidValue;
     const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+    if (a.staged) return hipErrorInvalidValue;  // launch32_staged
     if (a.kind == 0)
         hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kARows, false>), grid, block, 0, st, a);
     else if (a.img && a.fold && a.mixg)
@@ -83,10 +85,29 @@ inline hipError_t launch32(const FwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Single images staged through LDS (opt-in; bf16 input, P = 14, one frame size): the tile's pixel
+// rows are shared by the waves, so a wave takes TM = 2 row blocks and reads half the weight
+// fragments per product.
+template <int P, int ISZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD, int BD>
+inline hipError_t launch32_staged(const FwdArgs &a, hipStream_t st) {
+    constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+    if (a.tiles_m != (a.n_rows + BM - 1) / BM || a.tiles_n != (a.E + BN - 1) / BN) return hipErrorInvalidValue;
+    if (!a.staged || !a.img || a.fold || a.kind != 1) return hipErrorInvalidValue;
+    if constexpr (P == 14 && ISZ == 2) {
+        if (a.mixg) return hipErrorInvalidValue;  // one frame geometry per staged launch
+        hipLaunchKernelGGL((pe_fwd32_kernel<P, ISZ, OSZ, TM, TN, WM, WN, KS, PF, AD, BD, kAStaged, false>),
+                           dim3(a.tiles_m * a.tiles_n), dim3(WM * WN * 64), 0, st, a);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
 template <int P, int ISZ, int OSZ, int TM, int TN, int AD>
 inline hipError_t launch_sk(const FwdArgs &a, hipStream_t st) {
     constexpr int BM = TM * 32, BN = TN * 32;
     if (a.tiles_m != (a.n_rows + BM - 1) / BM || a.tiles_n != (a.E + BN - 1) / BN) return hipErrorInvalidValue;
+    if (a.staged) return hipErrorInvalidValue;  // the LDS-staged image path is the large-tile kernel's
     const dim3 grid(a.tiles_m * a.tiles_n), block(256);
     if (a.kind == 0)
         hipLaunchKernelGGL((pe_fwd32_sk_kernel<P, ISZ, OSZ, TM, TN, AD, kARows, false>), grid, block, 0, st, a);
@@ -122,6 +143,15 @@ inline hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
     } else {
         // 8 waves of 32 x BN (two per SIMD), one weight k-step per LDS buffer (a barrier per k-step
         // measured ~2% faster than two), eight weight fragments read ahead
+        if (a.staged) {
+            // staged single images: 8 waves of 64 x 128 (or 64 x 64), all of a k-step's weight
+            // fragments read ahead
+            switch (a.tiles) {
+                case kTileLarge256: return launch32_staged<P, ISZ, OSZ, 2, 4, 4, 2, 1, 8, 2, 3>(a, st);
+                case kTileLarge128: return launch32_staged<P, ISZ, OSZ, 2, 2, 4, 2, 1, 4, 2, 3>(a, st);
+                default: return hipErrorInvalidValue;
+            }
+        }
         switch (a.tiles) {
             case kTileLarge256: return launch32<P, ISZ, OSZ, 1, 8, 8, 1, 1, 8, 2, 3>(a, st);
             case kTileLarge128: return launch32<P, ISZ, OSZ, 1, 4, 8, 1, 1, 8, 2, 3>(a, st);

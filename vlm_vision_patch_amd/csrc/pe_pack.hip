@@ -73,9 +73,11 @@ __global__ void pe_pack_kernel(const TW *__restrict__ w, TW *__restrict__ wpk, i
         return;
     }
     if constexpr (esz == 2) {
-        // temporal-split map: g = 2j + tt, unique fragment uf = 2s + j
+        // temporal-split map: g = 2j + tt, unique fragment uf = 2s + j (kPackTTG: the grouped
+        // order's fragment 2s + j)
         const int tt = g & 1;
-        const UFrag f = tt_frag(P, 2 * s + (g >> 1));
+        const int ufg = 2 * s + (g >> 1);
+        const UFrag f = tt_frag(P, map == kPackTTG ? ttg_uf(P, ufg) : ufg);
 #pragma unroll
         for (int j = 0; j < epf; ++j) {
             int u = f.u1, x = f.x1 + j;

@@ -204,6 +204,12 @@ int plan_forward(const PlanRequest &r, std::vector<Launch> &out, std::string &er
             off += elems[i];
         }
         set_tiles(L, choose_tiles(L.a.n_rows, E, r.weight_esz, r.num_cus), E);
+        // opt-in: single images of one frame size with bf16 input and weight, P = 14, on the large
+        // tiles: the kernel stages the tile's pixel rows through LDS and reads the weight in the
+        // grouped order
+        L.a.staged = (r.stage_images && L.a.img && !L.a.fold && !L.a.mixg && P == 14 && r.weight_esz == 2 &&
+                      ies == 2 && (L.tile.id == kTileLarge256 || L.tile.id == kTileLarge128)) ? 1 : 0;
+        if (L.a.staged) L.weight_map = kWeightGrouped;
         out.push_back(L);
         x0 += span;
         i0 = i1;

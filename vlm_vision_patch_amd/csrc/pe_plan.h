@@ -44,6 +44,8 @@ struct FwdArgs {
     int32_t fold;          // 1: such a launch reads the folded weight (kAFold)
     int32_t mixg;          // 1: frames launch whose items differ in frame size (h, w)
     int32_t tiles;         // TileShape::id of the kernel and tile the plan chose
+    int32_t staged;        // 1: single images whose pixel rows the kernel stages through LDS
+                           //    (bf16 P = 14 large tiles; reads the grouped weight kWeightGrouped)
     uint32_t plane, rstr;  // channel and pixel-row strides (elements) when every item has one frame size
     // every item of the launch the same (t, h, w, F): item of a row by division, no table lookup
     int32_t uni;
@@ -66,7 +68,7 @@ struct TileShape {
 const char *kernel_name(int tile_id);
 
 // Packed weights a handle holds (pe_create packs each once).
-enum WeightMap { kWeightFrames = 0, kWeightRows = 1, kWeightFold = 2 };
+enum WeightMap { kWeightFrames = 0, kWeightRows = 1, kWeightFold = 2, kWeightGrouped = 3 };
 
 struct PlanRequest {
     int P, E, m;           // patch size, embed dim, merge size
@@ -74,6 +76,7 @@ struct PlanRequest {
     int in_esz, out_esz;   // bytes per input / output element
     int merge;             // frames rows in merge-window order
     int image_fold;        // approximate fold of single-frame items (bf16 weight)
+    int stage_images;      // opt-in LDS-staged gather of single images (bf16, P = 14, large tiles)
     int num_cus;           // compute units of the device (0: assume 256)
     int input_kind;        // 0 patch rows, 1 frames (pe_input_kind)
     const int32_t *grid_thw;
