@@ -43,10 +43,12 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     // the weight fragments per product. A row is written at least two k-steps before the first
     // read of it (the per-step barrier in between publishes it) and into a group buffer only
     // after the last read of the group it held. Patch pitch 240 bytes (14 fragments + 16): the 16
-    // lanes of a 16-byte read land on distinct banks.
+    // lanes of a 16-byte read land on distinct banks. Opt-in (pe_config.stage_images): on gfx950
+    // these whole-row loads take more texture-data cycles per byte than the register gather's,
+    // and the path measured 3-20 % slower.
     constexpr bool SG = AM == kAStaged;
-    static_assert(!SG || (P == 14 && ISZ == 2 && S == 37 && BM == 32 * WM * WN && KS == 1),
-                  "LDS-staged images: bf16, P = 14, one 32-row slice per wave, a barrier per k-step");
+    static_assert(!SG || (P == 14 && ISZ == 2 && S == 37 && BM == 32 * WM * WN && KS == 1 && !MG),
+                  "LDS-staged images: bf16, P = 14, one frame geometry, one 32-row slice per wave, a barrier per k-step");
     constexpr int SG_PITCH = 240;
     constexpr int SG_BLOCK = BM * SG_PITCH;        // one group of the tile's patches
     constexpr int SGOFF = 2 * KBUF;                // after the weight buffers
@@ -155,29 +157,18 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     };
 
     // LDS-staged images: pixel row u of the lane's patch in the wave's slice (part 0: px 0..7,
-    // part 1: px 6..13); the per-row part of the address is a scalar for one frame geometry, per lane
-    // otherwise. Every byte read lies inside the patch's own pixel row (tail rows past the launch
-    // read patch 0).
-    // Loading lane L takes part L & 1 of patch L >> 1 of the slice: a quad of lanes reads two
-    // neighbouring patches' 56 contiguous bytes, and the two half-waves read different patches
-    // (were they to read the same cache lines, the loads would take about twice the time in the
-    // texture data path).
+    // part 1: px 6..13); the per-row part of the address is a scalar for one frame geometry.
+    // Every byte read lies inside the patch's own pixel row (tail rows past the launch read
+    // patch 0). Loading lane L takes part L & 1 of patch L >> 1 of the slice: a quad of lanes
+    // reads two neighbouring patches' 56 contiguous bytes, and the two half-waves read different
+    // patches (measured faster than each half-wave reading one part of all 32 patches).
     const int sgp = lane >> 1, sgh = lane & 1;
-    uint32_t sgv = 0u, sgpl = 0u, sgrs = 0u;
-    auto sg_setup = [&]() {
-        const PatchRef p = patch_of_row<P>(a, row0 + wave * 32 + sgp);
-        sgv = p.base * 2u + (sgh ? 12u : 0u);
-        sgpl = p.plane;
-        sgrs = p.rstr;
-    };
+    uint32_t sgv = 0u;
+    auto sg_setup = [&]() { sgv = patch_of_row<P>(a, row0 + wave * 32 + sgp).base * 2u + (sgh ? 12u : 0u); };
     auto sg_load = [&](auto uc) -> u32x4 {
         constexpr int u = decltype(uc)::value;
-        if constexpr (MG)
-            return __builtin_amdgcn_raw_buffer_load_b128(
-                rsrc, (int)(sgv + ((uint32_t)(u / P) * sgpl + (uint32_t)(u % P) * sgrs) * 2u), 0, 0);
-        else
-            return __builtin_amdgcn_raw_buffer_load_b128(
-                rsrc, (int)sgv, (int)(((uint32_t)(u / P) * plane + (uint32_t)(u % P) * rstr) * 2u), 0);
+        return __builtin_amdgcn_raw_buffer_load_b128(
+            rsrc, (int)sgv, (int)(((uint32_t)(u / P) * plane + (uint32_t)(u % P) * rstr) * 2u), 0);
     };
     // ... and its place in the group buffer (sg_row): the lane's patch slot
     const uint32_t sgw = SGOFF + (uint32_t)(wave * 32 + sgp) * SG_PITCH;
