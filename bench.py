@@ -623,8 +623,9 @@ def main():
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
         qai = q["flops"] / q["bytes"]
         qdom = max(q["plan"], key=lambda L: L["n_rows"])
-        also[q["wl"].name + ("_as_patch_rows" if as_rows else "") + ("_plus_pos_embed" if with_add else "")
-             + ("_image_fold_approx" if fold else "") + ("_lds_staged" if stage else "")] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
+        key = (q["wl"].name + ("_as_patch_rows" if as_rows else "") + ("_plus_pos_embed" if with_add else "")
+               + ("_image_fold_approx" if fold else "") + ("_lds_staged" if stage else ""))
+        also[key] = {"patches_per_s": round(q["n"] / qt, 1), "ms_per_step": round(q["ms"], 5),
                               "tflops": round(q["flops"] / qt / 1e12, 2),
                               "frac_matrix_peak": round(q["flops"] / qt / 1e12 / qpk, 4),
                               "frac_hbm": round(q["bytes"] / qt / 1e9 / PEAK_HBM_GBS, 4),
@@ -632,6 +633,8 @@ def main():
                               "frac_roofline_model": round(q["flops"] / qt / 1e12 / min(qpk, qai * PEAK_HBM_GBS / 1e3), 4),
                               "kernel": qdom["kernel"], "tile": qdom["tile"], "launches_per_step": len(q["plan"]),
                               "n_patches": q["n"], "steps": st,
+                              # HBM bytes per launch from committed counters on this kernel code, if any
+                              "traffic": load_traffic(qdom["kernel"], key) if len(q["plan"]) == 1 else None,
                               **({"approximate": "image fold: W[:, :, 0] + W[:, :, 1] rounded to bf16 once; "
                                                  "tflops counts the nominal Conv3d FLOPs, the matrix cores do "
                                                  "about half for images"} if fold else {})}
