@@ -538,6 +538,29 @@ def test_wide_embedding_large_tiles(pe):
     check(got, ref, od, "e4096 video")
 
 
+@pytest.mark.parametrize("E,items,dt", [
+    (65536, [(1, 4, 6, 1)], torch.bfloat16),            # the largest E pe_create accepts; split-k tiles
+    (65520, [(1, 4, 6, 1)], torch.bfloat16),            # E not a multiple of 32: a ragged last column block
+    (65536, [(1, 32, 64, 1)], torch.bfloat16),          # 2,048 rows: 256 x 256 tiles, 256 column tiles
+    (65520, [(1, 6, 4, 1), (2, 2, 4, 3)], torch.float32),   # fp32 weight and input, an image and a video
+])
+def test_embedding_at_the_limit(pe, E, items, dt):
+    """The widest embeddings pe_create accepts (E <= 65536, a multiple of 16), on sampled rows."""
+    P = 14
+    K = 3 * 2 * P * P
+    xs = [make(1400 + i, (F, 3, h * P, w * P), dt) for i, (t, h, w, F) in enumerate(items)]
+    x = torch.cat([a.reshape(-1) for a in xs])
+    w = make(1401, (E, 3, 2, P, P), dt, "uniform", 1 / math.sqrt(K))
+    b = make(1402, (E,), dt, "uniform", 1 / math.sqrt(K))
+    grid = [[t, h, ww] for (t, h, ww, F) in items]
+    frames = [F for (*_, F) in items]
+    n = sum(t * h * ww for (t, h, ww, F) in items)
+    rows = sampled_rows(n, 53, 64) if n > 64 else None
+    got, ref, od = run(pe, "e%d_%s" % (E, "bf16" if dt == torch.bfloat16 else "f32"), x, w, b, grid, frames,
+                       order="merge", rows=rows)
+    check(got, ref, od, "E = %d" % E)
+
+
 def test_many_items_split_launches(pe):
     """More items than one launch's item table holds: the library splits the launches."""
     P, E = 14, 256
