@@ -806,6 +806,67 @@ def test_staged_images_integer_exact(pe):
 
 
 # ---------------------------------------------------------------------------------------------
+# poisoned pixels: a NaN or an Inf makes exactly the rows of its own patch non-finite. A load that
+# reached past a patch's pixels (even against a zero weight: NaN * 0 is NaN) would poison others.
+# ---------------------------------------------------------------------------------------------
+
+POISON = {
+    # name: P, items (t, h, w, F), input kind, order, in/weight dtype, staged images, E
+    "images_merge": (14, [(1, 12, 20, 1), (1, 8, 8, 1)], "frames", "merge", torch.bfloat16, False, 1280),
+    "images_large_tiles": (14, [(1, 64, 64, 1)], "frames", "merge", torch.bfloat16, False, 1280),
+    "images_staged": (14, [(1, 64, 64, 1)], "frames", "merge", torch.bfloat16, True, 1280),
+    "video_raster": (14, [(4, 10, 12, 7)], "frames", "raster", torch.bfloat16, False, 640),
+    "p16_images": (16, [(1, 10, 14, 1)], "frames", "raster", torch.bfloat16, False, 1152),
+    "patch_rows": (14, [(1, 1, 3000)], "patches", "raster", torch.bfloat16, False, 1280),
+    "fp32_frames": (14, [(1, 6, 8, 1), (2, 4, 2, 4)], "frames", "merge", torch.float32, False, 640),
+}
+
+
+@pytest.mark.parametrize("case", sorted(POISON))
+def test_poisoned_pixels_stay_in_their_patch(pe, case):
+    P, items, kind, order, dt, staged, E = POISON[case]
+    K = 3 * 2 * P * P
+    rng = np.random.default_rng(5100)
+    w = make(5101, (E, 3, 2, P, P), dt, "uniform", 1 / math.sqrt(K))
+    b = make(5102, (E,), dt, "uniform", 1 / math.sqrt(K))
+    if kind == "patches":
+        n = items[0][2]
+        x = make(5103, (n, K), dt)
+        grid, frames = [[1, 1, n]], None
+        # a row's first and last elements, and one in the middle of another row
+        for r, k in ((5, 0), (5, K - 1), (777, K // 2), (n - 1, K - 1)):
+            x[r, k] = float("nan") if r != 777 else float("inf")
+    else:
+        xs = [make(5103 + i, (F, 3, h * P, ww * P), dt) for i, (t, h, ww, F) in enumerate(items)]
+        # per item: a few patches, each poisoned at one pixel on its edge (px 0 or P - 1, pixel
+        # row P - 1) in some channel and frame
+        for (t, h, ww, F), xi in zip(items, xs):
+            for _ in range(3):
+                f, c = int(rng.integers(F)), int(rng.integers(3))
+                hp, wp = int(rng.integers(h)), int(rng.integers(ww))
+                py, px = [(0, 0), (0, P - 1), (P - 1, 0), (P - 1, P - 1)][int(rng.integers(4))]
+                xi[f, c, hp * P + py, wp * P + px] = float("nan") if rng.random() < 0.5 else float("inf")
+        x = torch.cat([a.reshape(-1) for a in xs])
+        grid = [[t, h, ww] for (t, h, ww, F) in items]
+        frames = [F for (*_, F) in items]
+    say("poisoned pixels %s: %s" % (case, grid if len(grid) < 4 else "%d items" % len(grid)))
+    mod = pe.PatchEmbed(w.to(DEV), b.to(DEV), order=order, stage_images=staged)
+    if staged:
+        assert [L["a_mode"] for L in mod.plan(grid, frames)] == ["images_lds"]
+    out = mod(x.to(DEV), grid, frames, kind=kind)
+    torch.cuda.synchronize()
+    mod.close()
+    got = out.double().cpu().numpy()
+    ref = oracle.forward(x, w, b, grid=grid, frames=frames, kind=kind, order=order)
+    poisoned = ~np.isfinite(ref).all(axis=1)
+    assert poisoned.any() and not poisoned.all()
+    # the poisoned patches' rows are non-finite wherever the oracle's are; every other row is finite
+    # and within tolerance
+    assert np.array_equal(~np.isfinite(got).all(axis=1), poisoned)
+    check(got[~poisoned], ref[~poisoned], dt, "poisoned " + case)
+
+
+# ---------------------------------------------------------------------------------------------
 # empty input and error paths (validated before any launch)
 # ---------------------------------------------------------------------------------------------
 
