@@ -264,15 +264,18 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
     if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const int64_t row_bytes = (int64_t)cfg.embed_dim * rq.out_esz;
+    // every launch's packed weight is bound (and checked) before the first launch is queued
+    for (pe::Launch &L : plan) {
+        switch (L.weight_map) {
+            case pe::kWeightRows: L.a.wpk = h->wpk_rows; break;
+            case pe::kWeightFold: L.a.wpk = h->wpk_fold; break;
+            case pe::kWeightGrouped: L.a.wpk = h->wpk_grp; break;
+            default: L.a.wpk = h->wpk; break;
+        }
+        if (!L.a.wpk) return fail(PE_ERR_UNSUPPORTED, "the plan asks for a packed weight the handle does not hold");
+    }
     for (pe::Launch &L : plan) {
         pe::FwdArgs &a = L.a;
-        switch (L.weight_map) {
-            case pe::kWeightRows: a.wpk = h->wpk_rows; break;
-            case pe::kWeightFold: a.wpk = h->wpk_fold; break;
-            case pe::kWeightGrouped: a.wpk = h->wpk_grp; break;
-            default: a.wpk = h->wpk; break;
-        }
-        if (!a.wpk) return fail(PE_ERR_UNSUPPORTED, "the plan asks for a packed weight the handle does not hold");
         a.bias = h->bias32;
         a.in = static_cast<const char *>(input) + L.in_off;
         a.out = static_cast<char *>(out) + L.row0 * row_bytes;
