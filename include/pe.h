@@ -122,7 +122,7 @@ int pe_create(const pe_config *cfg, const void *weight, const void *bias, void *
  *   frames     HOST int32 [n_items] frame counts F_i for FRAMES input, or NULL: then an item
  *              with t = 1 is one image frame (F = 1) and an item with t > 1 has F = Tp*t.
  *              Requires ceil(F_i / Tp) == t_i. Ignored for PATCHES.
- *   n_items    number of items; 0 is a no-op that returns PE_OK.
+ *   n_items    number of items, at least 1 (0 items, N = 0, is PE_ERR_SHAPE).
  *   out        device [N, E] in the handle's out dtype; rows of item i follow those of i-1.
  * Arithmetic: products of the input and weight values accumulated in fp32 together with the
  * fp32 bias, one round-to-nearest-even cast to the output dtype. Allocates nothing; does not
@@ -190,7 +190,7 @@ typedef struct {
  *   h, input_kind, in_dtype, grid_thw, frames, n_items   as pe_forward (no device pointers needed).
  *   info       host array of max_info entries (may be NULL when max_info is 0); the first
  *              min(count, max_info) launches are written.
- * Returns the number of launches (0 for n_items == 0), or a negative pe_status: the same request
+ * Returns the number of launches (at least 1), or a negative pe_status: the same request
  * checks and codes as pe_forward, PE_ERR_INVALID_ARG for max_info < 0 or a NULL info with
  * max_info > 0.
  */

@@ -92,7 +92,7 @@ def model_plan(r):
     grid, frames = r["grid"], r["frames"]
     n = len(grid)
     if n == 0:
-        return PE_OK, []
+        return PE_ERR_SHAPE, []
     K = 6 * P * P
     fr_in = r["kind"] == 1
     merge = fr_in and r["merge"]

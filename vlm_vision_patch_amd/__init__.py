@@ -280,6 +280,8 @@ class PatchEmbed:
         workgroups, rows and input range per launch. Nothing is launched."""
         ik = PE_INPUT_PATCHES if kind == "patches" else PE_INPUT_FRAMES
         g = grid_thw.tolist() if hasattr(grid_thw, "tolist") else grid_thw
+        if len(g) == 0:
+            return []   # an empty batch launches nothing (the C ABI calls 0 items an error)
         return pe_forward_plan(self._h, ik, _dtype_code(in_dtype if in_dtype is not None else self.weight_dtype),
                                g, frames)
 

@@ -226,7 +226,7 @@ void fill_request(pe_handle h, int32_t input_kind, int32_t in_dtype, const int32
 int check_request(pe_handle h, int32_t input_kind, int32_t in_dtype, int32_t n_items, const int32_t *grid_thw) {
     if (!h) return fail(PE_ERR_INVALID_ARG, "handle is NULL");
     if (n_items < 0) return fail(PE_ERR_INVALID_ARG, "n_items must be >= 0 (got %d)", n_items);
-    if (n_items == 0) return PE_OK;
+    if (n_items == 0) return fail(PE_ERR_SHAPE, "no items: N = 0");
     if (!grid_thw) return fail(PE_ERR_INVALID_ARG, "grid_thw is NULL");
     if (input_kind != PE_INPUT_PATCHES && input_kind != PE_INPUT_FRAMES)
         return fail(PE_ERR_INVALID_ARG, "bad input_kind %d", input_kind);
@@ -245,7 +245,7 @@ int forward_impl(pe_handle h, int32_t input_kind, const void *input, int32_t in_
                  void *out, void *hip_stream) {
     if (!h) return fail(PE_ERR_INVALID_ARG, "handle is NULL");
     if (n_items < 0) return fail(PE_ERR_INVALID_ARG, "n_items must be >= 0 (got %d)", n_items);
-    if (n_items == 0) return PE_OK;
+    if (n_items == 0) return fail(PE_ERR_SHAPE, "no items: N = 0");
     if (!grid_thw) return fail(PE_ERR_INVALID_ARG, "grid_thw is NULL");
     if (!input) return fail(PE_ERR_INVALID_ARG, "input is NULL");
     if (!out) return fail(PE_ERR_INVALID_ARG, "out is NULL");
@@ -309,7 +309,6 @@ int pe_forward_plan(pe_handle h, int32_t input_kind, int32_t in_dtype, const int
         return fail(PE_ERR_INVALID_ARG, "info must hold max_info >= 0 entries");
     const int crc = check_request(h, input_kind, in_dtype, n_items, grid_thw);
     if (crc != PE_OK) return crc;
-    if (n_items == 0) return 0;
     pe::PlanRequest rq;
     fill_request(h, input_kind, in_dtype, grid_thw, frames, n_items, rq);
     std::vector<pe::Launch> plan;

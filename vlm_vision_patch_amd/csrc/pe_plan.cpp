@@ -76,7 +76,7 @@ TileShape choose_tiles(int64_t n_rows, int E, int weight_esz, int num_cus) {
 int plan_forward(const PlanRequest &r, std::vector<Launch> &out, std::string &err) {
     out.clear();
     if (r.n_items < 0) return fail(err, PE_ERR_INVALID_ARG, "n_items must be >= 0 (got %d)", r.n_items);
-    if (r.n_items == 0) return PE_OK;
+    if (r.n_items == 0) return fail(err, PE_ERR_SHAPE, "no items: N = 0");
     if (!r.grid_thw) return fail(err, PE_ERR_INVALID_ARG, "grid_thw is NULL");
     if (r.input_kind != PE_INPUT_PATCHES && r.input_kind != PE_INPUT_FRAMES)
         return fail(err, PE_ERR_INVALID_ARG, "bad input_kind %d", r.input_kind);

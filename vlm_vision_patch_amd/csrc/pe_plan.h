@@ -95,7 +95,7 @@ struct Launch {
 
 // Validate the grid and plan the launches. Returns 0 (PE_OK) with the launches in order, or a
 // negative pe_status (PE_ERR_INVALID_ARG, PE_ERR_SHAPE, PE_ERR_UNSUPPORTED) with a message in err
-// and no launches. n_items == 0 plans nothing.
+// and no launches. n_items == 0 (N = 0) is PE_ERR_SHAPE.
 int plan_forward(const PlanRequest &r, std::vector<Launch> &out, std::string &err);
 
 // Tile for a launch of n_rows output rows (see pe_plan.cpp for the cost model).
