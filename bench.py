@@ -306,6 +306,23 @@ def time_merger_front(idx, steps, warmup=3, reps=5, eps=1e-6, eager=False):
             "steps": steps}
 
 
+def time_linear(a, w2, b2, steps):
+    """Milliseconds per torch.nn.functional.linear(a, w2, b2) (hipBLASLt), K eager calls between
+    events after three untimed ones."""
+    import torch
+    for _ in range(3):
+        y = torch.nn.functional.linear(a, w2, b2)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        y = torch.nn.functional.linear(a, w2, b2)
+    e1.record()
+    torch.cuda.synchronize()
+    del y
+    return e0.elapsed_time(e1) / steps
+
+
 def time_linear_context(idx, steps=20):
     """hipBLASLt (torch.nn.functional.linear) on the same product with the patches already
     flattened into a contiguous [N, K] matrix: context for the gather-fused kernel, not a target."""
@@ -319,20 +336,27 @@ def time_linear_context(idx, steps=20):
     a = workloads.random_tensor((n, wl.k), seed=2000 + idx, dtype=dt).to(dev)
     w2 = w.reshape(wl.embed, wl.k).to(dev)
     b2 = b.to(dev) if b is not None else None
-    for _ in range(3):
-        y = torch.nn.functional.linear(a, w2, b2)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        y = torch.nn.functional.linear(a, w2, b2)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    del y, a
+    ms = time_linear(a, w2, b2, steps)
+    del a
     return {"what": "torch.nn.functional.linear (hipBLASLt) on a contiguous [N, K] patch matrix, same "
                     "N, K, E, dtype and bias; the patchify gather not included", "ms_per_step": round(ms, 5),
             "tflops": round(2.0 * n * wl.k * wl.embed / (ms / 1e3) / 1e12, 2), "steps": steps}
+
+
+def time_square_context(m=8192, steps=20):
+    """hipBLASLt on an m x m x m bf16 product: what the vendor library reaches on a large square
+    product on this chip, a practical ceiling for bf16 matrix-core work next to the nominal peak."""
+    import torch
+    import workloads
+    dev = torch.device("cuda:0")
+    a = workloads.random_tensor((m, m), seed=3001, dtype=torch.bfloat16).to(dev)
+    w2 = workloads.random_tensor((m, m), seed=3002, dtype=torch.bfloat16).to(dev)
+    ms = time_linear(a, w2, None, steps)
+    del a, w2
+    tf = 2.0 * m ** 3 / (ms / 1e3) / 1e12
+    return {"what": "torch.nn.functional.linear (hipBLASLt) on a %d x %d x %d bf16 product, no bias" % (m, m, m),
+            "ms_per_step": round(ms, 5), "tflops": round(tf, 2), "frac_matrix_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "steps": steps}
 
 
 def cpu_info():
@@ -640,6 +664,7 @@ def main():
                                                  "about half for images"} if fold else {})}
     if not args.no_context and not args.eager:
         also["context_library_gemm_" + workloads_name(5)] = time_linear_context(5)
+        also["context_library_gemm_square_8192"] = time_square_context()
     cpu, parity = cpu_baseline(r) if cpu_leg else (None, None)
     line = {
         "metric": METRIC, "value": round(r["n"] / t_s, 1), "unit": "patches/s", "n_gpus": 1,
