@@ -16,12 +16,10 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     constexpr int STAGE = BN * 64;                  // packed-weight bytes of one k-step
     constexpr int CH = (STAGE / 16 + NT - 1) / NT;  // 16-byte chunks per thread per k-step
     constexpr bool CH_EVEN = (STAGE / 16) % NT == 0;
-    // epilogue staging: EPR rows of a wave's tile at a time (16, or 8 where 16 rows of every wave
-    // would not fit the LDS), fp32; a pitch of 8 mod 16 dwords puts the two lane halves (rows 4
-    // apart) on disjoint banks
+    // epilogue staging: 16 rows of a wave's tile at a time, fp32; a pitch of 8 mod 16 dwords
+    // puts the two lane halves (rows 4 apart) on disjoint banks
     constexpr int EP_PITCH = TN * 32 + 8;           // dwords
-    constexpr int EPR = 16 * EP_PITCH * 4 * WM * WN <= 160 * 1024 ? 16 : 8;
-    constexpr int EP_WAVE = EPR * EP_PITCH * 4;     // bytes per wave
+    constexpr int EP_WAVE = 16 * EP_PITCH * 4;      // bytes per wave
     constexpr int KBUF = KS * STAGE;
     // Patch rows stage A through LDS as well: each row's k-steps are 128-byte pieces of one
     // contiguous row, loaded by consecutive threads (eight rows per load instruction, every
@@ -382,15 +380,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     float *ep = reinterpret_cast<float *>(lds + wave * EP_WAVE);
     constexpr int VPC = 16 / OSZ;                 // output values per 16-byte chunk
     constexpr int RCH = TN * 32 / VPC;            // chunks per row
-    constexpr int CHUNKS = EPR * RCH;             // chunks in EPR rows
+    constexpr int CHUNKS = 16 * RCH;              // chunks in 16 rows
     const int wcol0 = col0 + wn * TN * 32;
-    // A fused bf16 addend is read one EPR-row block ahead, so its latency overlaps the staging and
+    // A fused bf16 addend is read one 16-row block ahead, so its latency overlaps the staging and
     // the stores of the block before; an fp32 one (twice the registers) is read at the start of its
     // own block and overlaps that block's staging. Chunks outside the output read the addend's
     // first chunk.
-    constexpr int CPL = (CHUNKS + 63) / 64;       // chunks per lane in EPR rows
-    constexpr int NPART = 32 / EPR;               // EPR-row parts of a 32-row block
-    constexpr int NBLK = NPART * TM;              // EPR-row blocks per wave
+    constexpr int CPL = (CHUNKS + 63) / 64;       // chunks per lane in 16 rows
+    constexpr int NBLK = 2 * TM;                  // 16-row blocks per wave
     constexpr int NBUF = OSZ == 2 ? 2 : 1;
     const bool has_add = a.addend != nullptr;
     auto add_load = [&](int it, u32x4 (&dst)[CPL]) {
@@ -398,7 +395,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
         for (int jj = 0; jj < CPL; ++jj) {
             const int c = jj * 64 + lane;
             const int r = c / RCH, qq = c % RCH;
-            const int row = row0 + (wm * TM + it / NPART) * 32 + (it % NPART) * EPR + r, col = wcol0 + qq * VPC;
+            const int row = row0 + (wm * TM + it / 2) * 32 + (it % 2) * 16 + r, col = wcol0 + qq * VPC;
             const bool ok = (CHUNKS % 64 == 0 || c < CHUNKS) && row < a.n_rows && col < a.E;
             dst[jj] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.addend) +
                                                        (ok ? ((int64_t)row * a.E + col) * OSZ : 0));
@@ -408,7 +405,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     if (NBUF == 2 && has_add) add_load(0, adq[0]);
 #pragma unroll
     for (int it = 0; it < NBLK; ++it) {
-        const int rb = it / NPART, part = it % NPART;
+        const int rb = it / 2, half = it % 2;
         if (has_add) {
             if (NBUF == 1) add_load(it, adq[0]);
             else if (it + 1 < NBLK) add_load(it + 1, adq[(it + 1) % NBUF]);
@@ -416,14 +413,14 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
 #pragma unroll
         for (int cb = 0; cb < TN; ++cb)
 #pragma unroll
-            for (int q = 0; q < EPR / 2; ++q) {
-                const int i = part * (EPR / 2) + q;
-                const int rl = 8 * (q / 4) + 4 * h + (q % 4);   // row within these EPR
+            for (int q = 0; q < 8; ++q) {
+                const int i = half * 8 + q;
+                const int rl = 8 * (q / 4) + 4 * h + (q % 4);   // row within these 16
                 ep[rl * EP_PITCH + cb * 32 + l32] = acc[rb][cb][i];
             }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's writes are in LDS
         __builtin_amdgcn_wave_barrier();
-        const int rbase = row0 + (wm * TM + rb) * 32 + part * EPR;
+        const int rbase = row0 + (wm * TM + rb) * 32 + half * 16;
 #pragma unroll
         for (int jj = 0; jj < CPL; ++jj) {
             const int c = jj * 64 + lane;
