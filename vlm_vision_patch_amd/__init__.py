@@ -14,7 +14,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libpe.so")
+# PE_LIB_PATH names another build of the same library, e.g. the LDS sentinel debug build
+# libpe_sentinel.so (build.py); by default the package's libpe.so
+LIB_PATH = os.environ.get("PE_LIB_PATH") or os.path.join(_PKG, "libpe.so")
 
 PE_OK, PE_ERR_INVALID_ARG, PE_ERR_SHAPE, PE_ERR_UNSUPPORTED, PE_ERR_HIP, PE_ERR_OOM = 0, -1, -2, -3, -4, -5
 PE_F32, PE_BF16 = 0, 1

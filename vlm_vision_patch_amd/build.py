@@ -2,6 +2,10 @@
 
 The forward kernels are split over translation units (one per patch size and input dtype) that
 compile in parallel; the objects are then linked into one shared library.
+
+build(sentinel=True) builds the same sources with -DPE_LDS_SENTINEL=1 into libpe_sentinel.so, a
+debug library whose kernels fill their LDS with NaN before use (csrc/pe_device.h); the tests run
+parity cases on it to catch LDS reads that come before their writes.
 """
 from __future__ import annotations
 
@@ -15,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpe.so")
+LIB_SENTINEL = os.path.join(PKG, "libpe_sentinel.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "pe_api.cpp"), os.path.join(CSRC, "pe_plan.cpp")]
 HEADERS = sorted(glob.glob(os.path.join(CSRC, "*.h"))) + [os.path.join(ROOT, "include", "pe.h")]
@@ -32,10 +37,10 @@ def link_cmd(objs, out: str):
     return ["/opt/rocm/bin/hipcc", "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", out]
 
 
-def stale() -> bool:
-    if not os.path.exists(LIB):
+def stale(lib: str = LIB) -> bool:
+    if not os.path.exists(lib):
         return True
-    t = os.path.getmtime(LIB)
+    t = os.path.getmtime(lib)
     return any(os.path.getmtime(p) > t for p in SOURCES + HEADERS + [__file__])
 
 
@@ -46,13 +51,15 @@ def _run(cmd):
     return res.returncode, msgs
 
 
-def build(force: bool = True, verbose: bool = False, jobs: int = 0) -> str:
-    if not force and not stale():
-        return LIB
+def build(force: bool = True, verbose: bool = False, jobs: int = 0, sentinel: bool = False) -> str:
+    lib = LIB_SENTINEL if sentinel else LIB
+    if not force and not stale(lib):
+        return lib
     os.makedirs(OBJDIR, exist_ok=True)
-    tag = "%d" % os.getpid()
+    tag = ("s%d" if sentinel else "%d") % os.getpid()
     objs = [os.path.join(OBJDIR, os.path.basename(s) + "." + tag + ".o") for s in SOURCES]
-    cmds = [compile_cmd(s, o) for s, o in zip(SOURCES, objs)]
+    extra = ["-DPE_LDS_SENTINEL=1"] if sentinel else []
+    cmds = [compile_cmd(s, o, extra) for s, o in zip(SOURCES, objs)]
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)), 8)
     try:
         with ThreadPoolExecutor(jobs) as ex:
@@ -64,19 +71,22 @@ def build(force: bool = True, verbose: bool = False, jobs: int = 0) -> str:
                 raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
             if verbose and msgs:
                 print("\n".join(msgs), flush=True)
-        tmp = LIB + ".tmp" + tag
+        tmp = lib + ".tmp" + tag
         rc, msgs = _run(link_cmd(objs, tmp))
         if rc != 0:
             raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
-        os.replace(tmp, LIB)
+        os.replace(tmp, lib)
     finally:
         for o in objs:
             if os.path.exists(o):
                 os.remove(o)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
     build(force=True, verbose=True)
     print(LIB)
+    if "--sentinel" in sys.argv[1:]:
+        build(force=True, verbose=True, sentinel=True)
+        print(LIB_SENTINEL)
     sys.exit(0)

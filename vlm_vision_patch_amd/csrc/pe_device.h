@@ -20,6 +20,26 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // gfx9 buffer descriptor word 3: 32-bit data format, raw (untyped) access.
 constexpr int kBufWord3 = 0x00020000;
 
+// LDS sentinel debug build (compiled with -DPE_LDS_SENTINEL=1 into libpe_sentinel.so; the shipped
+// libpe.so has it off and its machine code does not change): every kernel that uses LDS first
+// fills all of it with all-ones bytes, which are NaN as bf16 and as fp32, and waits at a barrier.
+// LDS keeps whatever an earlier workgroup left there, so a read of a slot that this workgroup
+// has not written yet (a missing write, or a read that runs ahead of its write) would otherwise
+// give a stale finite value; with the fill it puts a NaN into the output, which the parity
+// checks catch.
+#ifndef PE_LDS_SENTINEL
+#define PE_LDS_SENTINEL 0
+#endif
+template <int BYTES, int NT>
+__device__ __forceinline__ void lds_sentinel_fill(unsigned char *lds) {
+    if constexpr (PE_LDS_SENTINEL != 0) {
+        static_assert(BYTES % 16 == 0, "the fill writes 16-byte chunks");
+        for (int i = (int)threadIdx.x; i < BYTES / 16; i += NT)
+            reinterpret_cast<u32x4 *>(lds)[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+        __syncthreads();
+    }
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }

@@ -24,6 +24,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd16_kernel(const FwdArgs 
     constexpr int KBUF = KS * STAGE;            // one LDS buffer: KS k-steps of packed weight
     constexpr int LDS_BYTES = (2 * KBUF > EP_WAVE * WM * WN) ? 2 * KBUF : EP_WAVE * WM * WN;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    lds_sentinel_fill<LDS_BYTES, NT>(lds);
 
     // ---- tile: blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous run of
     // tiles so the tiles that share rows (same tm) run on one XCD, close in time.

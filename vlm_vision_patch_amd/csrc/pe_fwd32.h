@@ -56,6 +56,7 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     constexpr int LDS_BYTES = (MAIN_BYTES > EP_WAVE * WM * WN) ? MAIN_BYTES : EP_WAVE * WM * WN;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    lds_sentinel_fill<LDS_BYTES, NT>(lds);
 
     // ---- tile: blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous run of
     // tiles so the tiles that share rows (same tm) run on one XCD, close in time.

@@ -18,6 +18,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd32_sk_kernel(const FwdArgs a) {
     constexpr int PITCH = BN + 8;                   // dwords per partial-tile row (8 mod 16)
     constexpr int PART = BM * PITCH * 4;            // bytes per wave's partial tile
     __shared__ __attribute__((aligned(16))) unsigned char lds[NW * PART];
+    lds_sentinel_fill<NW * PART, NW * 64>(lds);
 
     const int G = a.tiles_m * a.tiles_n;
     const int bid = blockIdx.x;
