@@ -122,8 +122,8 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     add: fuse the add of a synthetic [N, E] tensor (position embeddings) into the epilogue.
     fold: the approximate image-fold mode (single-frame items on W[:, :, 0] + W[:, :, 1] in bf16).
     stage: the opt-in LDS-staged gather of single images (stage_images).
-    keep_out: also return the output of the last timed step (and the inputs, on the host), for the
-    parity check of the timed output.
+    keep_out: also return the output of the last timed step (and the inputs and the addend, on the
+    host), for the parity check of the timed output.
     The result holds the library's launch plan of one step (pe_forward_plan): which kernel runs,
     its tile and grid."""
     import torch
@@ -142,7 +142,7 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     if rows:
         x = workloads.random_tensor((n, wl.k), seed=1000 + idx, dtype=workloads.DTYPES[wl.in_dtype])
         kind, grid, frames = "patches", [[1, 1, n]], None
-    host_in = (x, w, b) if keep_out else None
+    host_in = (x, w, b, None) if keep_out else None
     x, w = x.to(dev), w.to(dev)
     b = b.to(dev) if b is not None else None
     mod = pe.PatchEmbed(w, b, order=wl.order, out_dtype=workloads.DTYPES[wl.out_dtype], image_fold=fold,
@@ -151,8 +151,11 @@ def time_workload(idx, steps, warmup, graph=True, rows=False, items=None, reps=1
     out = torch.empty((n, wl.embed), dtype=workloads.DTYPES[wl.out_dtype], device=dev)
     addend = None
     if add:
-        addend = (workloads.random_tensor((n, wl.embed), seed=3000 + idx) * 0.02).to(
-            workloads.DTYPES[wl.out_dtype]).to(dev)
+        addend_host = (workloads.random_tensor((n, wl.embed), seed=3000 + idx) * 0.02).to(
+            workloads.DTYPES[wl.out_dtype])
+        addend = addend_host.to(dev)
+        if keep_out:
+            host_in = host_in[:3] + (addend_host,)
     s = torch.cuda.Stream(device=dev)   # default priority
     with torch.cuda.stream(s):
         for _ in range(warmup):
@@ -417,6 +420,13 @@ def sample_rows(n, count, tile=256, seed=0):
     return sorted(picked)
 
 
+def _tolerance(wl, ref):
+    import numpy as np
+    if wl.out_dtype == "bf16":
+        return 1e-3 + 1e-2 * np.abs(ref), "|err| <= 1e-3 + 1e-2 |ref|"
+    return 5e-4, "|err| <= 5e-4"
+
+
 def cpu_baseline(r, target_seconds=15.0):
     """The oracle, as it stands, timed on this host over a bounded sample of the workload's output
     rows (about `target_seconds` of CPU work, on every core this process may use), and the same rows
@@ -424,7 +434,7 @@ def cpu_baseline(r, target_seconds=15.0):
     import numpy as np
     import oracle
     wl = r["wl"]
-    x, w, b = r["host_in"]
+    x, w, b, _ = r["host_in"]
     info = cpu_info()
     threads = info["usable"]
     n = r["n"]
@@ -453,10 +463,7 @@ def cpu_baseline(r, target_seconds=15.0):
     import torch
     got = r["out"].index_select(0, torch.tensor(rows, device=r["out"].device)).float().cpu().double().numpy()
     err = np.abs(got - ref)
-    if wl.out_dtype == "bf16":
-        tol, tol_text = 1e-3 + 1e-2 * np.abs(ref), "|err| <= 1e-3 + 1e-2 |ref|"
-    else:
-        tol, tol_text = 5e-4, "|err| <= 5e-4"
+    tol, tol_text = _tolerance(wl, ref)
     bad = int((err > tol).sum())
     sample = ("%s %d of the %d output rows of %s (drawn from a stratified sample: the first and last rows, both "
               "sides of 256-row tile edges, the rest spread evenly): fp64 direct Conv3d, %d threads, %.1f s" % (
@@ -468,6 +475,37 @@ def cpu_baseline(r, target_seconds=15.0):
     parity = {"rows_checked": len(rows), "max_abs_err": float(err.max()), "out_of_tolerance": bad,
               "tolerance": tol_text}
     return cpu, parity
+
+
+def cpu_baseline_config(q, max_rows=8192, approximate=False):
+    """Part of the cpu_baseline leg for a secondary line: the oracle timed on all output rows of the
+    line's last timed step, or on `max_rows` stratified rows of a larger one, and those rows of the
+    timed output compared with it. approximate: the image-fold line, whose sums differ from the
+    exact Conv3d by the folded weight's rounding; its error is reported with no tolerance."""
+    import numpy as np
+    import torch
+    import oracle
+    wl = q["wl"]
+    x, w, b, addend = q["host_in"]
+    threads = cpu_info()["usable"]
+    n = q["n"]
+    rows = sample_rows(n, min(n, max_rows), seed=5)
+    t0 = time.perf_counter()
+    ref = oracle.forward(x, w, b, grid=q["grid"], frames=q["frames"], kind=q["kind"], order=wl.order,
+                         rows=rows, addend=addend, threads=threads)
+    el = time.perf_counter() - t0
+    got = q["out"].index_select(0, torch.tensor(rows, device=q["out"].device)).float().cpu().double().numpy()
+    err = np.abs(got - ref)
+    out = {"rows_checked": len(rows), "of_rows": n, "oracle_s": round(el, 3),
+           "oracle_patches_per_s": round(len(rows) / el, 1), "cores": threads, "max_abs_err": float(err.max())}
+    if approximate:
+        out["out_of_tolerance"] = None
+        out["tolerance"] = "none: approximate mode, compared with the exact Conv3d"
+    else:
+        tol, tol_text = _tolerance(wl, ref)
+        out["out_of_tolerance"] = int((err > tol).sum())
+        out["tolerance"] = tol_text
+    return out
 
 
 def load_traffic(kernel, workload):
@@ -631,6 +669,7 @@ def main():
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
             "frac_roofline_model": round(tflops / min(peak_fl, ai * PEAK_HBM_GBS / 1e3), 4)}
     also = {}
+    per_config = {}
     for spec in [v.strip() for v in args.extra.split(",") if v.strip()]:
         if spec.endswith("n"):
             e = int(spec[:-1])
@@ -642,7 +681,7 @@ def main():
             continue
         st = max(5, min(args.steps, 50))
         q = time_workload(e, st, 3, graph=not args.eager, rows=as_rows, items=share, reps=3, add=with_add,
-                          fold=fold, stage=stage)
+                          fold=fold, stage=stage, keep_out=cpu_leg)
         qt = q["ms"] / 1e3
         qpk = PEAK_BF16_TFLOPS if q["wl"].w_dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
         qai = q["flops"] / q["bytes"]
@@ -662,10 +701,16 @@ def main():
                               **({"approximate": "image fold: W[:, :, 0] + W[:, :, 1] rounded to bf16 once; "
                                                  "tflops counts the nominal Conv3d FLOPs, the matrix cores do "
                                                  "about half for images"} if fold else {})}
+        if cpu_leg:
+            # the cpu_baseline leg for this line: oracle time and parity of its timed output
+            per_config[key] = cpu_baseline_config(q, approximate=fold)
+        del q
     if not args.no_context and not args.eager:
         also["context_library_gemm_" + workloads_name(5)] = time_linear_context(5)
         also["context_library_gemm_square_8192"] = time_square_context()
     cpu, parity = cpu_baseline(r) if cpu_leg else (None, None)
+    if cpu is not None:
+        cpu["per_config"] = per_config
     line = {
         "metric": METRIC, "value": round(r["n"] / t_s, 1), "unit": "patches/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms"], 6),
