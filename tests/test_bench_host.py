@@ -142,3 +142,27 @@ def test_kernel_code_hash_follows_the_code(tmp_path):
     assert after["pe_fwd16_kernel"] != hs["pe_fwd16_kernel"]
     assert {k: v for k, v in after.items() if k != "pe_fwd16_kernel"} == \
         {k: v for k, v in hs.items() if k != "pe_fwd16_kernel"}
+
+
+def test_cpu_leg_parity_of_a_secondary_line():
+    """cpu_baseline_config on a small frames line whose 'timed output' is made on the host: the
+    oracle's own rows rounded to bf16 pass; one element moved by 0.1 fails the tolerance; the
+    approximate line reports its error with no tolerance."""
+    import numpy as np
+    import torch
+    import oracle
+    wl = workloads.Workload(0, "tiny", "frames", "bf16", "bf16", "bf16", 14, 64, True, "merge",
+                            ((1, 4, 6),), (1,), (1, 3, 56, 84))
+    x, w, b = workloads.generate(wl)
+    grid, frames = [[1, 4, 6]], [1]
+    ref = oracle.forward(x, w, b, grid=grid, frames=frames, kind="frames", order="merge")
+    out = torch.from_numpy(ref).to(torch.bfloat16)
+    q = dict(wl=wl, n=24, host_in=(x, w, b, None), grid=grid, frames=frames, kind="frames", out=out)
+    r = bench.cpu_baseline_config(q, max_rows=10)
+    assert r["rows_checked"] == 10 and r["of_rows"] == 24 and r["out_of_tolerance"] == 0
+    assert r["max_abs_err"] <= np.abs(ref).max() * 2 ** -8
+    bad = out.clone()
+    bad[0, 3] += 0.1
+    assert bench.cpu_baseline_config(dict(q, out=bad), max_rows=24)["out_of_tolerance"] == 1
+    a = bench.cpu_baseline_config(dict(q, out=bad), max_rows=24, approximate=True)
+    assert a["out_of_tolerance"] is None and a["max_abs_err"] >= 0.09
