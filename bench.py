@@ -84,14 +84,20 @@ def kernel_symbols(b, kernel):
 def kernel_code_hash(kernel: str, lib: str = LIBPE) -> str:
     """Hash of the machine code of every instantiation of pe::`kernel` in the built library (each
     symbol's name and bytes, in name order). It keys HBM-traffic counters to the code they were
-    taken on: a change to that kernel's code changes it; a comment or another kernel does not."""
+    taken on: a change to that kernel's code changes it; a comment or another kernel does not.
+    A descriptor's entry offset (bytes 16-23 of the 64-byte `.kd`: the distance from the
+    descriptor to the code) is left out, since it moves when another kernel of the same code object
+    changes size."""
     b = open(lib, "rb").read()
     syms = sorted(kernel_symbols(b, kernel))
     if not syms:
         raise ValueError("no code for kernel %s in %s" % (kernel, lib))
     h = hashlib.sha256()
     for name, off, size in syms:
-        h.update(name.encode() + b"\0" + b[off: off + size])
+        body = b[off: off + size]
+        if name.endswith(".kd") and size == 64:
+            body = body[:16] + bytes(8) + body[24:]
+        h.update(name.encode() + b"\0" + body)
     return h.hexdigest()[:16]
 
 

@@ -142,6 +142,19 @@ def test_kernel_code_hash_follows_the_code(tmp_path):
     assert after["pe_fwd16_kernel"] != hs["pe_fwd16_kernel"]
     assert {k: v for k, v in after.items() if k != "pe_fwd16_kernel"} == \
         {k: v for k, v in hs.items() if k != "pe_fwd16_kernel"}
+    # a descriptor's entry offset (its distance to the code, which moves with the layout of the
+    # code object) does not count; its other fields (resources) do
+    kd_name, kd_off, kd_size = next((n, o, z) for n, o, z in sorted(syms) if n.endswith(".kd"))
+    assert kd_size == 64
+    moved = bytearray(b)
+    moved[kd_off + 16] ^= 0x40
+    lib3 = tmp_path / "libpe_moved.so"
+    lib3.write_bytes(bytes(moved))
+    assert bench.kernel_code_hash("pe_fwd16_kernel", str(lib3)) == hs["pe_fwd16_kernel"]
+    moved[kd_off + 16] ^= 0x40
+    moved[kd_off + 0] ^= 0x01          # group_segment_fixed_size: the LDS it asks for
+    lib3.write_bytes(bytes(moved))
+    assert bench.kernel_code_hash("pe_fwd16_kernel", str(lib3)) != hs["pe_fwd16_kernel"]
 
 
 def test_cpu_leg_parity_of_a_secondary_line():

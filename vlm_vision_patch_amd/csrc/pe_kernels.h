@@ -36,7 +36,9 @@
 // bf16 split-k kernel (pe_fwd32_sk_kernel), for few rows: four waves share a 32 x 160 (or 128)
 // tile, each over a quarter of the k-steps, partial tiles summed through LDS.
 //
-// fp32 kernel (pe_fwd16_kernel): the same structure with 16x16 blocks and v_mfma_f32_16x16x4_f32.
+// fp32 kernel (pe_fwd16_kernel): split-k like the bf16 split-k kernel, with 16x16 blocks and
+// v_mfma_f32_16x16x4_f32: four waves share a 32 x 160 (or 128) tile, each over a quarter of the
+// k-steps, the weight straight from global memory into registers.
 //
 // Rows of a tile are output rows in output order; each lane maps its row back to the patch
 // (item, tp, hp, wp) through the raster or merge-window order, so the order costs only index
@@ -52,13 +54,12 @@ namespace pe {
 // ----------------------------------------------------------------------------------------
 // Launchers
 // ----------------------------------------------------------------------------------------
-template <int P, int ESZ, int OSZ, int TM, int TN, int WM, int WN, int KS, int PF, int AD>
+template <int P, int ESZ, int OSZ, int TM, int TN, int AD>
 inline hipError_t launch16(const FwdArgs &a, hipStream_t st) {
-    constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
+    constexpr int BM = TM * 16, BN = TN * 16;
     if (a.tiles_m != (a.n_rows + BM - 1) / BM || a.tiles_n != (a.E + BN - 1) / BN) return hipErrorInvalidValue;
     if (a.staged) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((pe_fwd16_kernel<P, ESZ, OSZ, TM, TN, WM, WN, KS, PF, AD>), dim3(a.tiles_m * a.tiles_n),
-                       dim3(WM * WN * 64), 0, st, a);
+    hipLaunchKernelGGL((pe_fwd16_kernel<P, ESZ, OSZ, TM, TN, AD>), dim3(a.tiles_m * a.tiles_n), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -134,12 +135,12 @@ inline hipError_t launch_p(const FwdArgs &a, hipStream_t st) {
     // counts from their own template shapes and refuse a launch whose shape differs
     const int skn = a.E % 160 == 0 ? 160 : 128;
     if constexpr (ESZ == 4) {
-        // fp32 I/O: 16x16 blocks, small tiles (its fully unrolled k loop has 74 steps); 32 x 160
-        // tiles where E allows (1024 x 1280 makes 256 of them: one round, where 32 x 128 tiles
-        // take 1.25; measured 38 us against 45-47 us), one weight k-step per LDS buffer
+        // fp32 I/O: 16x16 blocks, split-k over four waves, small tiles; 32 x 160 tiles where E
+        // allows (1024 x 1280 makes 256 of them: one round, where 32 x 128 tiles take 1.25),
+        // loads two k-steps ahead
         if (a.tiles != kTileF32) return hipErrorInvalidValue;
-        if (skn == 160) return launch16<P, ESZ, OSZ, 1, 5, 2, 2, 1, 2, 2>(a, st);
-        return launch16<P, ESZ, OSZ, 1, 4, 2, 2, 2, 2, 2>(a, st);
+        if (skn == 160) return launch16<P, ESZ, OSZ, 2, 10, 2>(a, st);
+        return launch16<P, ESZ, OSZ, 2, 8, 2>(a, st);
     } else {
         // 8 waves of 32 x BN (two per SIMD), one weight k-step per LDS buffer (a barrier per k-step
         // measured ~2% faster than two), eight weight fragments read ahead
