@@ -1,6 +1,7 @@
 // pe_device.h -- device helpers shared by the gfx950 kernels: 16-byte vector types, the raw
-// buffer descriptor word, bf16 rounding, the output stores (with the optional fused addend) and
-// a compile-time loop.
+// buffer descriptor word, the LDS sentinel fill of the debug build, bf16 rounding, the output
+// stores (with the optional fused addend), the XCD-aware tile order, the split-k epilogue and a
+// compile-time loop.
 #pragma once
 
 #include <type_traits>
@@ -89,6 +90,58 @@ __device__ __forceinline__ void store_chunk(void *out, const void *addend, int64
     u32x4 ad = u32x4{0u, 0u, 0u, 0u};
     if (addend) ad = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(addend) + elem * OSZ);
     store_chunk_r<OSZ>(out, addend != nullptr, ad, elem, v);
+}
+
+// Tile of workgroup blockIdx.x: blocks are dealt to the 8 XCDs round-robin, so each XCD gets a
+// contiguous run of the launch's tiles. Row-major runs (row tiles outermost) keep the column
+// tiles that share a row tile's pixels on one XCD, close in time; column-major runs (a.colmajor,
+// for launches whose input is smaller than the weight) keep tiles that share weight columns
+// together instead.
+struct TileIdx { int tm, tn; };
+__device__ __forceinline__ TileIdx xcd_tile(const FwdArgs &a) {
+    const int G = a.tiles_m * a.tiles_n;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, loc = bid >> 3;
+    const int per = G >> 3, rem = G & 7;
+    const int L = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+    return TileIdx{a.colmajor ? L % a.tiles_m : L / a.tiles_n, a.colmajor ? L / a.tiles_m : L % a.tiles_n};
+}
+
+// Split-k epilogue: each of the NW waves left a BM x BN fp32 partial tile in LDS (wave w's at
+// byte w*PART, rows PITCH dwords apart). Wave `wave` sums rows [wave*BM/NW, (wave+1)*BM/NW) of
+// the NW partials in a fixed order (deterministic), adds `bias` (fp32 [E]) when it is given, and
+// stores 16-byte row-contiguous chunks: one RNE cast, the fused addend (if any) added first.
+template <int OSZ, int BM, int BN, int NW, int PITCH, int PART>
+__device__ __forceinline__ void sum_partials_store(const unsigned char *lds, const FwdArgs &a, int row0, int col0,
+                                                   int wave, int lane, const float *bias) {
+    constexpr int VPC = 16 / OSZ;                   // output values per 16-byte chunk
+    constexpr int RCH = BN / VPC;                   // chunks per row
+    constexpr int ROWS = BM / NW;                   // rows per wave
+    constexpr int CHUNKS = ROWS * RCH;
+    const float *p0 = reinterpret_cast<const float *>(lds);
+#pragma unroll
+    for (int jj = 0; jj < (CHUNKS + 63) / 64; ++jj) {
+        const int c = jj * 64 + lane;
+        if (CHUNKS % 64 != 0 && c >= CHUNKS) break;
+        const int r = wave * ROWS + c / RCH, q = c % RCH;
+        const int row = row0 + r, col = col0 + q * VPC;
+        if (row < a.n_rows && col < a.E) {
+            float v[VPC];
+#pragma unroll
+            for (int e4 = 0; e4 < VPC; e4 += 4) {
+                f32x4 t = *reinterpret_cast<const f32x4 *>(p0 + r * PITCH + q * VPC + e4);
+#pragma unroll
+                for (int w = 1; w < NW; ++w)
+                    t += *reinterpret_cast<const f32x4 *>(p0 + w * (PART / 4) + r * PITCH + q * VPC + e4);
+                v[e4] = t.x; v[e4 + 1] = t.y; v[e4 + 2] = t.z; v[e4 + 3] = t.w;
+            }
+            if (bias) {
+#pragma unroll
+                for (int e = 0; e < VPC; ++e) v[e] += bias[col + e];
+            }
+            store_chunk<OSZ>(a.out, a.addend, (int64_t)row * a.E + col, v);
+        }
+    }
 }
 
 // Compile-time loop: f(IC<0>{}), f(IC<1>{}), ..., f(IC<N-1>{}).

@@ -29,18 +29,8 @@ __global__ void __launch_bounds__(256, 1) pe_fwd16_kernel(const FwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[NW * PART];
     lds_sentinel_fill<NW * PART, NW * 64>(lds);
 
-    // ---- tile: blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous run of
-    // tiles so the tiles that share rows (same tm) run on one XCD, close in time.
-    const int G = a.tiles_m * a.tiles_n;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, loc = bid >> 3;
-    const int per = G >> 3, rem = G & 7;
-    const int L = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
-    // row-major runs share rows (A) within an XCD; column-major runs share weight columns, for
-    // launches whose input is smaller than the weight
-    const int tm = a.colmajor ? L % a.tiles_m : L / a.tiles_n;
-    const int tn = a.colmajor ? L / a.tiles_m : L % a.tiles_n;
-    const int row0 = tm * BM, col0 = tn * BN;
+    const TileIdx tile = xcd_tile(a);   // XCD-aware tile order (pe_gather.h)
+    const int row0 = tile.tm * BM, col0 = tile.tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -179,34 +169,7 @@ __global__ void __launch_bounds__(256, 1) pe_fwd16_kernel(const FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) part[(rb * 16 + 4 * g + i) * PITCH + cb * 16 + l16] = acc[rb][cb][i];
     __syncthreads();
-    constexpr int VPC = 16 / OSZ;                   // output values per 16-byte chunk
-    constexpr int RCH = BN / VPC;                   // chunks per row
-    constexpr int ROWS = BM / NW;                   // rows per wave
-    constexpr int CHUNKS = ROWS * RCH;
-    const float *p0 = reinterpret_cast<const float *>(lds);
-#pragma unroll
-    for (int jj = 0; jj < (CHUNKS + 63) / 64; ++jj) {
-        const int c = jj * 64 + lane;
-        if (CHUNKS % 64 != 0 && c >= CHUNKS) break;
-        const int r = wave * ROWS + c / RCH, q = c % RCH;
-        const int row = row0 + r, col = col0 + q * VPC;
-        if (row < a.n_rows && col < a.E) {
-            float v[VPC];
-#pragma unroll
-            for (int e4 = 0; e4 < VPC; e4 += 4) {
-                f32x4 t = *reinterpret_cast<const f32x4 *>(p0 + r * PITCH + q * VPC + e4);
-#pragma unroll
-                for (int w = 1; w < NW; ++w)
-                    t += *reinterpret_cast<const f32x4 *>(p0 + w * (PART / 4) + r * PITCH + q * VPC + e4);
-                v[e4] = t.x; v[e4 + 1] = t.y; v[e4 + 2] = t.z; v[e4 + 3] = t.w;
-            }
-            if (a.bias) {
-#pragma unroll
-                for (int e = 0; e < VPC; ++e) v[e] += a.bias[col + e];
-            }
-            store_chunk<OSZ>(a.out, a.addend, (int64_t)row * a.E + col, v);
-        }
-    }
+    sum_partials_store<OSZ, BM, BN, NW, PITCH, PART>(lds, a, row0, col0, wave, lane, a.bias);
 }
 
 }  // namespace pe

@@ -58,18 +58,8 @@ __global__ void __launch_bounds__(WM *WN * 64, 1) pe_fwd32_kernel(const FwdArgs 
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     lds_sentinel_fill<LDS_BYTES, NT>(lds);
 
-    // ---- tile: blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous run of
-    // tiles so the tiles that share rows (same tm) run on one XCD, close in time.
-    const int G = a.tiles_m * a.tiles_n;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, loc = bid >> 3;
-    const int per = G >> 3, rem = G & 7;
-    const int L = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
-    // row-major runs share rows (A) within an XCD; column-major runs share weight columns, for
-    // launches whose input is smaller than the weight
-    const int tm = a.colmajor ? L % a.tiles_m : L / a.tiles_n;
-    const int tn = a.colmajor ? L / a.tiles_m : L % a.tiles_n;
-    const int row0 = tm * BM, col0 = tn * BN;
+    const TileIdx tile = xcd_tile(a);   // XCD-aware tile order (pe_gather.h)
+    const int row0 = tile.tm * BM, col0 = tile.tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave - (wave / WN) * WN;
