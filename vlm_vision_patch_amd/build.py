@@ -51,42 +51,64 @@ def _run(cmd):
     return res.returncode, msgs
 
 
-def build(force: bool = True, verbose: bool = False, jobs: int = 0, sentinel: bool = False) -> str:
+def _jobs(sentinel: bool):
     lib = LIB_SENTINEL if sentinel else LIB
-    if not force and not stale(lib):
-        return lib
-    os.makedirs(OBJDIR, exist_ok=True)
     tag = ("s%d" if sentinel else "%d") % os.getpid()
     objs = [os.path.join(OBJDIR, os.path.basename(s) + "." + tag + ".o") for s in SOURCES]
     extra = ["-DPE_LDS_SENTINEL=1"] if sentinel else []
-    cmds = [compile_cmd(s, o, extra) for s, o in zip(SOURCES, objs)]
+    return lib, tag, objs, [compile_cmd(s, o, extra) for s, o in zip(SOURCES, objs)]
+
+
+def _build_many(variants, verbose: bool, jobs: int):
+    """Compile the objects of every (lib, tag, objs, cmds) in one pool (the largest translation
+    units first, so the long ones overlap), then link each library."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    cmds = [c for v in variants for c in v[3]]
+    order = sorted(range(len(cmds)), key=lambda i: -os.path.getsize(cmds[i][cmds[i].index("-c") + 1]))
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)), 8)
     try:
         with ThreadPoolExecutor(jobs) as ex:
-            results = list(ex.map(_run, cmds))
-        for cmd, (rc, msgs) in zip(cmds, results):
+            done = dict(zip(order, ex.map(_run, [cmds[i] for i in order])))
+        for i, cmd in enumerate(cmds):
+            rc, msgs = done[i]
             if verbose:
                 print(" ".join(cmd), flush=True)
             if rc != 0:
                 raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
             if verbose and msgs:
                 print("\n".join(msgs), flush=True)
-        tmp = lib + ".tmp" + tag
-        rc, msgs = _run(link_cmd(objs, tmp))
-        if rc != 0:
-            raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
-        os.replace(tmp, lib)
+        for lib, tag, objs, _ in variants:
+            tmp = lib + ".tmp" + tag
+            rc, msgs = _run(link_cmd(objs, tmp))
+            if rc != 0:
+                raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
+            os.replace(tmp, lib)
     finally:
-        for o in objs:
-            if os.path.exists(o):
-                os.remove(o)
-    return lib
+        for v in variants:
+            for o in v[2]:
+                if os.path.exists(o):
+                    os.remove(o)
+
+
+def build(force: bool = True, verbose: bool = False, jobs: int = 0, sentinel: bool = False) -> str:
+    """libpe.so (or, with sentinel, libpe_sentinel.so)."""
+    v = _jobs(sentinel)
+    if force or stale(v[0]):
+        _build_many([v], verbose, jobs)
+    return v[0]
+
+
+def build_all(force: bool = True, verbose: bool = False, jobs: int = 0):
+    """libpe.so and libpe_sentinel.so, compiled in one pool."""
+    vs = [v for v in (_jobs(False), _jobs(True)) if force or stale(v[0])]
+    if vs:
+        _build_many(vs, verbose, jobs)
+    return LIB, LIB_SENTINEL
 
 
 if __name__ == "__main__":
-    build(force=True, verbose=True)
-    print(LIB)
     if "--sentinel" in sys.argv[1:]:
-        build(force=True, verbose=True, sentinel=True)
-        print(LIB_SENTINEL)
+        print("\n".join(build_all(force=True, verbose=True)))
+    else:
+        print(build(force=True, verbose=True))
     sys.exit(0)
